@@ -1,0 +1,95 @@
+/*
+ * iqattn_oracle.h -- CPU oracle of the integer-only attention core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This oracle exists to check the HIP path.  Only
+ * the test-suite, the smoke check and the CPU-baseline leg of the benchmark
+ * may load it; the product library never includes, links or calls it, and it
+ * shares no code, header, table or helper with the product.
+ *
+ * What it computes (all integers, every step in the order of the pages):
+ *   I-ViT: Integer-only Quantization for Efficient Vision Transformer
+ *   Inference (mer.run summary of the paper):
+ *     sec. 3.2 "Dyadic Arithmetic for Linear Operations":  Q.K^T in integers,
+ *       then the dyadic requantisation (b * acc) >> c to int8 logits;
+ *     sec. 3.3 "Integer-only Softmax: Shiftmax":  subtract the row max,
+ *       multiply by log2(e) as x + (x>>1) - (x>>4), split into an integer
+ *       power q and a remainder r, 2^x by a linear piece and a right shift,
+ *       integer row sum, IntDiv to k_out-bit probabilities;
+ *     sec. 3.1 "Overview":  Attn = Softmax(Q K^T / sqrt(d)) V, uniform
+ *       symmetric quantiser (int8 range +-127).
+ *   FQ-ViT: Post-Training Quantization for Fully Quantized Vision Transformer
+ *   (IJCAI 2022 record), abstract:  Log-Int-Softmax, attention map quantised
+ *     to 4-bit log2 codes, P.V by the BitShift operator.
+ *   Trio-ViT (cloud.tencent.com article), sec. IV "Log2 Quantization for
+ *     Divisors in MSAs" (Eq. 11):  integer log2 by a leading-one detector
+ *     plus the next lower bit;  sec. V, requantisation module (Eq. 12):
+ *     b and c positive integers.
+ *
+ * Readings taken where the pages are silent, garbled or ambiguous are listed
+ * next to the code that takes them (R1..R22 in the comments of the .c file).
+ * Parity unpinned: the readings themselves (I0 = 1/S_logit, the extra exponent
+ * fraction bits n, M, the clamp of P at 2^(k_out-1)-1, floor requantisation,
+ * bias added to the int32 accumulator, the midpoint of the log2 rounding, the
+ * Q15 LIS accumulation) are choices; no number printed on the pages fixes
+ * them.  The tests pin the implementation of each choice and the whole
+ * pipeline against float64 softmax.
+ */
+#ifndef IQATTN_ORACLE_H
+#define IQATTN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t batch, heads, seq_len, head_dim;
+  int32_t qk_b, qk_c;         /* dyadic pair of the Q.K^T requantisation     */
+  int32_t pv_b, pv_c;         /* dyadic pair of the P.V requantisation       */
+  int32_t i0;                 /* integer 1.0 at the logit scale (S = 1/i0)   */
+  int32_t exp_frac_bits;      /* n: extra fraction bits of the integer 2^x   */
+  int32_t intdiv_m;           /* M of IntDiv                                 */
+  int32_t k_out;              /* Shiftmax output bits                        */
+  int32_t variant;            /* 0 = Shiftmax, 1 = Log-Int-Softmax           */
+  int32_t lis_bits;           /* LIS code bits                               */
+  int32_t window;             /* w > 0: relative bias table present, N = w*w */
+  const int32_t* rel_bias;    /* [heads][(2w-1)^2], or NULL                  */
+} orc_params;
+
+/* Optional per-head dumps of the intermediates, for heads [begin, end) in
+ * the flattened (b * heads + h) order.  Any pointer may be NULL.             */
+typedef struct {
+  int64_t* acc;     /* [nh][N][N]  Q.K^T (+ bias)                    */
+  int32_t* logit;   /* [nh][N][N]  int8 logits L                     */
+  int64_t* expv;    /* [nh][N][N]  integer exponentials e            */
+  int64_t* rowsum;  /* [nh][N]     row sums s                        */
+  int64_t* prob;    /* [nh][N][N]  P (Shiftmax) or Ph (LIS)          */
+  int32_t* code;    /* [nh][N][N]  LIS codes                         */
+  int64_t* pv;      /* [nh][N][d]  P.V accumulator o                 */
+} orc_dump;
+
+int orc_check_params(const orc_params* p);
+
+/* Full pipeline for heads [head_begin, head_end).  q, k, v, out are whole
+ * [B, H, N, d] int8 tensors (row-major); out is written for those heads only.
+ * Returns 0, or a negative value for invalid parameters.                      */
+int orc_forward(const orc_params* p, const int8_t* q, const int8_t* k,
+                const int8_t* v, int8_t* out, int64_t head_begin,
+                int64_t head_end, const orc_dump* dump);
+
+/* Steps exposed one at a time for the tests. */
+int32_t orc_requant(int64_t x, int32_t b, int32_t c);
+void    orc_requant_array(const int64_t* x, int64_t n, int32_t b, int32_t c,
+                          int32_t* out);
+int64_t orc_shift_exp(int32_t delta, int32_t i0, int32_t n);
+int32_t orc_ilog2r(int64_t x);
+/* Shiftmax / LIS on one row of int8 logits (steps after the requantisation). */
+int orc_softmax_row(const orc_params* p, const int32_t* logits, int32_t n,
+                    int64_t* e_out, int64_t* s_out, int64_t* prob_out,
+                    int32_t* code_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

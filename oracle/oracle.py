@@ -1,0 +1,171 @@
+"""ctypes binding of the C oracle (iqattn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Builds liboracle.so with plain gcc -O2 (no
+intrinsics, no threads) and marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "iqattn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle (single-threaded, -O2, C99)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC",
+                               "-shared", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "batch", "heads", "seq_len", "head_dim", "qk_b", "qk_c", "pv_b", "pv_c",
+        "i0", "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "window")] + \
+        [("rel_bias", C.POINTER(C.c_int32))]
+
+
+class _Dump(C.Structure):
+    _fields_ = [("acc", C.POINTER(C.c_int64)), ("logit", C.POINTER(C.c_int32)),
+                ("expv", C.POINTER(C.c_int64)), ("rowsum", C.POINTER(C.c_int64)),
+                ("prob", C.POINTER(C.c_int64)), ("code", C.POINTER(C.c_int32)),
+                ("pv", C.POINTER(C.c_int64))]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = C.CDLL(_LIB)
+        lib.orc_check_params.argtypes = [C.POINTER(_Params)]
+        lib.orc_forward.argtypes = [C.POINTER(_Params), C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_int64, C.c_int64, C.POINTER(_Dump)]
+        lib.orc_requant.argtypes = [C.c_int64, C.c_int32, C.c_int32]
+        lib.orc_requant.restype = C.c_int32
+        lib.orc_requant_array.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
+                                          C.c_void_p]
+        lib.orc_shift_exp.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+        lib.orc_shift_exp.restype = C.c_int64
+        lib.orc_ilog2r.argtypes = [C.c_int64]
+        lib.orc_ilog2r.restype = C.c_int32
+        lib.orc_softmax_row.argtypes = [C.POINTER(_Params), C.c_void_p, C.c_int32,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def _make_params(shape, params: Dict[str, object]):
+    B, H, N, d = shape
+    p = _Params()
+    p.batch, p.heads, p.seq_len, p.head_dim = B, H, N, d
+    for name in ("qk_b", "qk_c", "pv_b", "pv_c", "i0", "exp_frac_bits", "intdiv_m",
+                 "k_out", "variant", "lis_bits", "window"):
+        setattr(p, name, int(params.get(name, 0) or 0))
+    keep = None
+    rb = params.get("rel_bias")
+    if rb is not None:
+        keep = np.ascontiguousarray(np.asarray(rb, dtype=np.int32))
+        p.rel_bias = keep.ctypes.data_as(C.POINTER(C.c_int32))
+    return p, keep
+
+
+def check_params(shape, params) -> int:
+    p, _keep = _make_params(shape, params)
+    return _load().orc_check_params(C.byref(p))
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, params: Dict[str, object],
+            heads: Optional[tuple] = None, dump: bool = False):
+    """Run the oracle on int8 [B, H, N, d] tensors.
+
+    heads = (begin, end) restricts the work to flattened heads [begin, end);
+    the returned `out` is then shaped [end - begin, N, d].  With dump=True a
+    dict of intermediates for those heads is returned as well.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    k = np.ascontiguousarray(k, dtype=np.int8)
+    v = np.ascontiguousarray(v, dtype=np.int8)
+    B, H, N, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    p, keep = _make_params(q.shape, params)
+    total = B * H
+    h0, h1 = (0, total) if heads is None else heads
+    out = np.zeros((B, H, N, d), dtype=np.int8)
+    dumps = None
+    dstruct = None
+    if dump:
+        nh = h1 - h0
+        dumps = dict(acc=np.zeros((nh, N, N), np.int64), logit=np.zeros((nh, N, N), np.int32),
+                     expv=np.zeros((nh, N, N), np.int64), rowsum=np.zeros((nh, N), np.int64),
+                     prob=np.zeros((nh, N, N), np.int64), code=np.zeros((nh, N, N), np.int32),
+                     pv=np.zeros((nh, N, d), np.int64))
+        dstruct = _Dump(_ptr(dumps["acc"], C.c_int64), _ptr(dumps["logit"], C.c_int32),
+                        _ptr(dumps["expv"], C.c_int64), _ptr(dumps["rowsum"], C.c_int64),
+                        _ptr(dumps["prob"], C.c_int64), _ptr(dumps["code"], C.c_int32),
+                        _ptr(dumps["pv"], C.c_int64))
+    rc = lib.orc_forward(C.byref(p), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                         out.ctypes.data, h0, h1, C.byref(dstruct) if dstruct else None)
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle rejected the parameters (code {rc})")
+    res = out.reshape(total, N, d)[h0:h1]
+    return (res, dumps) if dump else res
+
+
+def softmax_row(logits, params: Dict[str, object]):
+    """Shiftmax / LIS on one row of int8 logits -> (e, s, prob, code)."""
+    lib = _load()
+    L = np.ascontiguousarray(np.asarray(logits, dtype=np.int32))
+    n = L.shape[0]
+    p, keep = _make_params((1, 1, n, 1), params)
+    e = np.zeros(n, np.int64)
+    s = np.zeros(1, np.int64)
+    prob = np.zeros(n, np.int64)
+    code = np.zeros(n, np.int32)
+    rc = lib.orc_softmax_row(C.byref(p), L.ctypes.data, n, e.ctypes.data, s.ctypes.data,
+                             prob.ctypes.data, code.ctypes.data)
+    del keep
+    if rc != 0:
+        raise ValueError(f"oracle softmax_row failed ({rc})")
+    return e, int(s[0]), prob, code
+
+
+def requant(x: int, b: int, c: int) -> int:
+    return int(_load().orc_requant(int(x), int(b), int(c)))
+
+
+def requant_array(x: np.ndarray, b: int, c: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.int64)
+    out = np.zeros(x.shape, np.int32)
+    _load().orc_requant_array(x.ctypes.data, x.size, int(b), int(c), out.ctypes.data)
+    return out
+
+
+def shift_exp(delta: int, i0: int, n: int) -> int:
+    return int(_load().orc_shift_exp(int(delta), int(i0), int(n)))
+
+
+def ilog2r(x: int) -> int:
+    return int(_load().orc_ilog2r(int(x)))

@@ -1,0 +1,68 @@
+"""Brute-force evaluator of the integer attention pipeline, for tiny shapes.
+
+Written independently of the C oracle with Python's unbounded integers and
+exact rationals: every floor is math.floor of a Fraction, the q/r split is
+divmod, the leading-one index is int.bit_length.  It pins the oracle's
+integer mechanics (widths, shifts, signs, loops); the readings themselves are
+pinned elsewhere (softmax bound, closed forms, worked examples).
+"""
+from fractions import Fraction
+from math import floor
+
+
+def fl(num, den=1):
+    return floor(Fraction(num, den))
+
+
+def requant(x, b, c):
+    return max(-127, min(127, fl(b * x, 2 ** c)))
+
+
+def shift_exp(delta, i0, n):
+    ip = delta + fl(delta, 2) - fl(delta, 16)
+    q, r = divmod(-ip, i0)
+    mant = i0 + fl(-r, 2)
+    return fl(mant * 2 ** n, 2 ** q)
+
+
+def ilog2r(x):
+    k = x.bit_length() - 1
+    return k + ((x >> (k - 1)) & 1 if k >= 1 else 0)
+
+
+def softmax_row(L, p):
+    m = max(L)
+    e = [shift_exp(x - m, p["i0"], p["exp_frac_bits"]) for x in L]
+    s = sum(e)
+    f = fl(2 ** p["intdiv_m"], s)
+    if p["variant"] == 0:
+        pmax = 2 ** (p["k_out"] - 1) - 1
+        w = [min(fl(f * x, 2 ** (p["intdiv_m"] - p["k_out"] + 1)), pmax) for x in e]
+        return e, w, None
+    F = 2 ** p["lis_bits"] - 1
+    ph = [fl(f * x, 2 ** (p["intdiv_m"] - F)) for x in e]
+    codes = [F if v == 0 else max(0, min(F, F - ilog2r(v))) for v in ph]
+    return e, [2 ** (F - c) for c in codes], codes
+
+
+def attention(q, k, v, p):
+    """q, k, v: nested lists / arrays [B][H][N][d] of ints.  Returns out."""
+    B, H, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    w = p.get("window", 0) or 0
+    out = [[[[0] * d for _ in range(N)] for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                L = []
+                for j in range(N):
+                    acc = sum(int(q[b][h][i][t]) * int(k[b][h][j][t]) for t in range(d))
+                    if w:
+                        dr = i // w - j // w
+                        dc = i % w - j % w
+                        acc += int(p["rel_bias"][h][(dr + w - 1) * (2 * w - 1) + dc + w - 1])
+                    L.append(requant(acc, p["qk_b"], p["qk_c"]))
+                _, wts, _ = softmax_row(L, p)
+                for t in range(d):
+                    o = sum(wts[j] * int(v[b][h][j][t]) for j in range(N))
+                    out[b][h][i][t] = requant(o, p["pv_b"], p["pv_c"])
+    return out
