@@ -1,0 +1,185 @@
+"""Benchmark of the fused integer-only attention on one MI355X.
+
+A step is one fused launch over the whole batch of the ViT-B/DeiT-B-shaped
+workload (B=128, H=12, N=197, d=64, seeded synthetic int8 inputs already
+resident in HBM).  Prints one JSON line:
+  value      int8 TOPS = 4 N^2 d B H / (time per step)  (both contractions,
+             a multiply-accumulate counted as 2 ops)
+  roofline   achieved HBM GB/s of the fused kernel (algorithmic bytes
+             4 N d per head: Q, K, V read once, Out written once) against the
+             8 TB/s peak; the per-launch duration comes from HIP events
+             around every launch on the launch stream
+  traffic    HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE,
+             read from profiles/ when recorded for the current kernel source
+  cpu_baseline  the CPU oracle (single thread) on the same inputs
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
+KERNEL_SRC = os.path.join(ROOT, "integer_only_quantized_int8_amd", "csrc", "iqattn.hip")
+METRIC = "integer-only MSA int8 TOPS + % roofline, B=128 H=12 N=197 d=64, 1 MI355X"
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload shape 0..4 (2 = headline)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads timed on the CPU oracle (0 = all heads, at most ~30 s)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from integer_only_quantized_int8_amd import workloads as W
+    from integer_only_quantized_int8_amd.iqattn import IQAttn
+
+    t0 = time.time()
+    w = W.config_workload(args.config)
+    B, H, N, d = w.q.shape
+    heads = B * H
+    print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    out = torch.empty_like(q)
+    att = IQAttn(w.q.shape, w.params)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        att.forward(q, k, v, out)
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, HIP events around every launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        att.forward(q, k, v, out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_ms = wall * 1e3 / args.steps
+    kern_ms = float(launch_ms.mean())
+
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    gpu_out = out.cpu().numpy()
+    ops = 4.0 * N * N * d * heads
+    alg_bytes = 4.0 * N * d * heads
+    if w.params.get("rel_bias") is not None:
+        alg_bytes += np.asarray(w.params["rel_bias"]).nbytes
+    tops = ops / (step_ms * 1e-3) / 1e12
+    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    traffic = None
+    trec = load_traffic(w.name)
+    if trec is not None:
+        traffic = trec["hbm_bytes_per_launch"]
+
+    result = {
+        "metric": METRIC if args.config == 2 else f"integer-only MSA int8 TOPS, {w.name}",
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded int8 Q/K/V, ViT-B/DeiT-B-shaped; no dataset or weights)",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
+                   "variant": "lis" if w.params["variant"] == 1 else "shiftmax",
+                   "seed": 1000 + args.config, "parallelism": "none (1 GPU)"},
+        "kernel_us_mean": round(kern_ms * 1e3, 3),
+        "kernel_us_min": round(float(launch_ms.min()) * 1e3, 3),
+        "heads_per_s": round(heads / (step_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(alg_bytes),
+                     "mfma_int8": {"achieved_tops": round(ops / (kern_ms * 1e-3) / 1e12, 2),
+                                   "peak_tops": MFMA_I8_PEAK_TOPS,
+                                   "frac": round(ops / (kern_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}},
+    }
+
+    if not args.no_cpu:
+        import oracle
+        if not os.path.exists(oracle.library_path()):
+            oracle.build()
+        per_head_guess = 0.006 * (N / 197.0) ** 2 * (d / 64.0)
+        n_cpu = args.cpu_heads or min(heads, max(1, int(30.0 / per_head_guess)))
+        print(f"[bench] CPU oracle on {n_cpu} heads ...", file=sys.stderr, flush=True)
+        t1 = time.perf_counter()
+        ref = oracle.forward(w.q, w.k, w.v, w.params, heads=(0, n_cpu))
+        cpu_s = time.perf_counter() - t1
+        same = bool(np.array_equal(gpu_out.reshape(heads, N, d)[:n_cpu], ref))
+        result["cpu_baseline"] = {
+            "value": round(4.0 * N * N * d * n_cpu / cpu_s / 1e12, 6), "unit": "TOPS",
+            "cores": 1, "kind": "oracle",
+            "sample": f"heads 0..{n_cpu - 1} of {w.name} (seed {1000 + args.config}), "
+                      f"{cpu_s:.2f} s single-threaded C -O2 on {cpu_model()} "
+                      f"(host nproc {os.cpu_count()})",
+            "heads_per_s": round(n_cpu / cpu_s, 2)}
+        result["bit_exact_vs_oracle"] = {"heads_compared": n_cpu, "equal": same}
+    att.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+"""Thin ctypes binding of libiqattn.so (argument marshalling only).
+
+The four functions carry the C-ABI names and arguments of include/iqattn.h.
+Tensors are torch int8 tensors on the HIP device; streams are
+torch.cuda.Stream objects (HIP streams under ROCm) or None for the current
+stream.  Every step of the attention runs in the library's kernels; if the
+library is missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libiqattn.so")
+
+IQATTN_OK = 0
+IQATTN_E_INVAL = -1
+IQATTN_E_SHAPE = -2
+IQATTN_E_ALLOC = -3
+IQATTN_E_LAUNCH = -4
+IQATTN_E_NULL = -5
+IQATTN_E_ALIGN = -6
+IQATTN_E_DEVICE = -7
+IQATTN_SHIFTMAX = 0
+IQATTN_LIS = 1
+IQATTN_MAX_SEQ = 640
+
+EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror")
+
+
+class iqattn_params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "batch", "heads", "seq_len", "head_dim", "qk_b", "qk_c", "pv_b", "pv_c", "i0",
+        "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "window")] + \
+        [("rel_bias", C.POINTER(C.c_int32))]
+
+
+class IQAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {iqattn_strerror(code)} ({code})")
+
+
+_lib = None
+
+
+def load_library():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with integer_only_quantized_int8_amd/build.py "
+                "(hipcc --offload-arch=gfx950); there is no fallback path")
+        lib = C.CDLL(LIB_PATH)
+        lib.iqattn_create.argtypes = [C.POINTER(iqattn_params), C.POINTER(C.c_void_p)]
+        lib.iqattn_create.restype = C.c_int
+        lib.iqattn_forward.argtypes = [C.c_void_p] * 6
+        lib.iqattn_forward.restype = C.c_int
+        lib.iqattn_destroy.argtypes = [C.c_void_p]
+        lib.iqattn_destroy.restype = C.c_int
+        lib.iqattn_strerror.argtypes = [C.c_int]
+        lib.iqattn_strerror.restype = C.c_char_p
+        _lib = lib
+    return _lib
+
+
+def make_params(shape, params: Dict[str, object]):
+    """Fill an iqattn_params from (B, H, N, d) and a parameter dict.  Returns the
+    struct and the int32 array that backs rel_bias (keep it alive until create
+    returns)."""
+    B, H, N, d = shape
+    p = iqattn_params()
+    p.batch, p.heads, p.seq_len, p.head_dim = int(B), int(H), int(N), int(d)
+    for name in ("qk_b", "qk_c", "pv_b", "pv_c", "i0", "exp_frac_bits", "intdiv_m", "k_out",
+                 "variant", "lis_bits", "window"):
+        setattr(p, name, int(params.get(name, 0) or 0))
+    keep = None
+    rb = params.get("rel_bias")
+    if rb is not None:
+        keep = np.ascontiguousarray(np.asarray(rb, dtype=np.int32))
+        p.rel_bias = keep.ctypes.data_as(C.POINTER(C.c_int32))
+    return p, keep
+
+
+def iqattn_strerror(code: int) -> str:
+    return load_library().iqattn_strerror(int(code)).decode()
+
+
+def iqattn_create(p: iqattn_params) -> int:
+    """Returns the context handle (an integer address); raises IQAttnError."""
+    ctx = C.c_void_p()
+    rc = load_library().iqattn_create(C.byref(p), C.byref(ctx))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqattn_create")
+    return ctx.value
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def iqattn_forward(ctx: int, q, k, v, out, stream=None) -> None:
+    """Enqueue the fused attention on `stream` (default: torch's current stream)."""
+    rc = load_library().iqattn_forward(C.c_void_p(ctx), C.c_void_p(q.data_ptr()),
+                                       C.c_void_p(k.data_ptr()), C.c_void_p(v.data_ptr()),
+                                       C.c_void_p(out.data_ptr()),
+                                       C.c_void_p(_stream_handle(stream)))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqattn_forward")
+
+
+def iqattn_destroy(ctx: Optional[int]) -> None:
+    rc = load_library().iqattn_destroy(C.c_void_p(ctx) if ctx else None)
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqattn_destroy")
+
+
+class IQAttn:
+    """Owns one context for a fixed shape and parameter set."""
+
+    def __init__(self, shape, params: Dict[str, object]):
+        self.shape = tuple(int(x) for x in shape)
+        p, keep = make_params(self.shape, params)
+        self.ctx = iqattn_create(p)
+        del keep
+
+    def forward(self, q, k, v, out=None, stream=None):
+        import torch
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() \
+                    or tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} must be a contiguous int8 device tensor of shape "
+                                 f"{self.shape}")
+        if out is None:
+            out = torch.empty_like(q)
+        iqattn_forward(self.ctx, q, k, v, out, stream)
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if self.ctx:
+            iqattn_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,97 @@
+"""The C-ABI library: loads, exports every declared symbol, rejects bad
+parameters before touching a device (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from integer_only_quantized_int8_amd import iqattn as IQ
+from integer_only_quantized_int8_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(iqattn_\w+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(IQ.LIB_PATH):
+        from integer_only_quantized_int8_amd import build
+        build.build()
+    return IQ.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == set(IQ.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(os.path.join(ROOT, "include", "iqattn.h")).read()
+    for name in ("IQATTN_OK", "IQATTN_E_INVAL", "IQATTN_E_SHAPE", "IQATTN_E_ALLOC",
+                 "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
+                 "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_MAX_SEQ"):
+        m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(IQ, name), name
+
+
+def _create_rc(lib, shape, **over):
+    params = W.default_params(3)
+    params.update(over)
+    p, keep = IQ.make_params(shape, params)
+    ctx = C.c_void_p(12345)
+    rc = lib.iqattn_create(C.byref(p), C.byref(ctx))
+    del keep
+    return rc, ctx.value
+
+
+@pytest.mark.parametrize("shape,over,code", [
+    ((1, 1, 0, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 1, 641, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 1, 16, 48), {}, IQ.IQATTN_E_SHAPE),
+    ((-1, 1, 16, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 0, 16, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 1, 16, 64), {"qk_b": 0}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"pv_c": 63}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"i0": 0}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"i0": 16, "exp_frac_bits": 19}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"k_out": 9}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"intdiv_m": 32}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"variant": 2}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"variant": 1, "lis_bits": 5}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"variant": 1, "intdiv_m": 14}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"window": 4}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"window": 3, "rel_bias": np.zeros((1, 25), np.int32)}, IQ.IQATTN_E_SHAPE),
+    ((1, 1, 16, 64), {"window": 4, "rel_bias": np.full((1, 49), (1 << 30) + 1, np.int32)},
+     IQ.IQATTN_E_INVAL),
+])
+def test_create_rejects_bad_parameters_before_any_device_call(lib, shape, over, code):
+    rc, ctx = _create_rc(lib, shape, **over)
+    assert rc == code
+    assert ctx is None  # *out is cleared on every error
+
+
+def test_null_pointers_and_destroy_null(lib):
+    assert lib.iqattn_create(None, None) == IQ.IQATTN_E_NULL
+    p, _ = IQ.make_params((1, 1, 16, 64), W.default_params(1))
+    assert lib.iqattn_create(C.byref(p), None) == IQ.IQATTN_E_NULL
+    assert lib.iqattn_destroy(None) == IQ.IQATTN_OK
+    assert lib.iqattn_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL
+
+
+def test_strerror_texts(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        s = IQ.iqattn_strerror(code)
+        assert isinstance(s, str) and s

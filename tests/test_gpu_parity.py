@@ -1,0 +1,186 @@
+"""Bit-exact parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Every output is an integer, so the GPU result must equal the oracle byte for
+byte.  Full-size workloads are compared on every head the oracle finishes in
+seconds, and on sampled heads otherwise.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from integer_only_quantized_int8_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "no GPU visible"
+    return torch
+
+
+def run_gpu(torch, w, params=None, stream=None):
+    from integer_only_quantized_int8_amd.iqattn import IQAttn
+    params = w.params if params is None else params
+    att = IQAttn(w.q.shape, params)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(w.q).to(dev)
+    k = torch.from_numpy(w.k).to(dev)
+    v = torch.from_numpy(w.v).to(dev)
+    out = torch.full_like(q, 99)
+    att.forward(q, k, v, out, stream=stream)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    att.close()
+    return res
+
+
+def check(torch, w, params=None, heads=None, label=""):
+    params = w.params if params is None else params
+    _say(f"[parity] {label} {w.q.shape} variant={params['variant']} heads={heads}")
+    got = run_gpu(torch, w, params)
+    total = w.batch * w.heads
+    N, d = w.seq_len, w.head_dim
+    got = got.reshape(total, N, d)
+    if heads is None:
+        sel = np.arange(total)
+        ref = oracle.forward(w.q, w.k, w.v, params)
+        assert np.array_equal(got, ref), f"{label}: mismatch"
+        return
+    sel = heads
+    for u in sel:
+        ref = oracle.forward(w.q, w.k, w.v, params, heads=(int(u), int(u) + 1))[0]
+        if not np.array_equal(got[u], ref):
+            bad = np.argwhere(got[u] != ref)
+            raise AssertionError(f"{label}: head {u} differs at {len(bad)} entries, "
+                                 f"first {bad[:4].tolist()}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_config_full(torch_dev, cfg):
+    w = W.config_workload(cfg)
+    check(torch_dev, w, label=f"shape {cfg} seed {1000 + cfg}")
+
+
+def test_headline_config_all_heads(torch_dev):
+    w = W.config_workload(2)
+    check(torch_dev, w, label="shape 2 seed 1002 (all 1536 heads)")
+
+
+def test_lis_config_sampled_heads(torch_dev):
+    w = W.config_workload(4)
+    total = w.batch * w.heads
+    heads = sorted(set([0, 1, total - 1] + list(np.random.default_rng(0).choice(total, 9,
+                                                                            replace=False))))
+    check(torch_dev, w, heads=heads, label="shape 4 seed 1004 (sampled heads)")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_configs_other_seeds_reduced_batch(torch_dev, cfg, seed):
+    spec = dict(W.CONFIGS[cfg])
+    spec["batch"] = {0: 1, 1: 4, 2: 2, 3: 24, 4: 1}[cfg]
+    w = W.make_workload(seed=seed, **spec)
+    check(torch_dev, w, label=f"shape {cfg} seed {seed}")
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("N", [1, 2, 15, 16, 17, 31, 33, 49, 63, 64, 65, 130, 197, 208, 209,
+                               400, 577, 640])
+def test_edge_shapes(torch_dev, N, d, variant):
+    w = W.make_workload(2, 3, N, d, seed=N * 7 + d + variant, variant=variant)
+    check(torch_dev, w, label=f"edge N={N} d={d}")
+
+
+def test_all_equal_logits(torch_dev):
+    w = W.make_workload(2, 2, 197, 64, seed=5)
+    w.q[:] = 0
+    check(torch_dev, w, label="Q=0")
+    p = dict(w.params, variant=1, pv_c=28)
+    check(torch_dev, w, params=p, label="Q=0 LIS")
+
+
+def test_saturated_logits_and_dyadic_extremes(torch_dev):
+    w = W.make_workload(2, 2, 197, 64, seed=6, sigma=127.0)
+    for qk_b, qk_c in ((1 << 14, 22), ((1 << 15) - 1, 22), ((1 << 15) - 1, 12), (1, 1),
+                       ((1 << 31) - 1, 30)):
+        p = dict(w.params, qk_b=qk_b, qk_c=qk_c)
+        check(torch_dev, w, params=p, label=f"qk b={qk_b} c={qk_c}")
+    for pv_b, pv_c in ((1 << 14, 20), ((1 << 15) - 1, 20), ((1 << 31) - 1, 40)):
+        p = dict(w.params, pv_b=pv_b, pv_c=pv_c)
+        check(torch_dev, w, params=p, label=f"pv b={pv_b} c={pv_c}")
+
+
+def test_outlier_rows_and_bias(torch_dev):
+    w = W.make_workload(2, 3, 197, 64, seed=9, per_head_sigma=(8.0, 40.0), k_outlier_p=0.05)
+    check(torch_dev, w, label="outliers")
+    w = W.make_workload(5, 2, 49, 32, seed=10, window=7, bias_range=4000)
+    check(torch_dev, w, label="large bias")
+    w = W.make_workload(2, 2, 64, 64, seed=11, window=8)
+    check(torch_dev, w, label="bias w=8 d=64")
+
+
+@pytest.mark.parametrize("over", [dict(i0=1, exp_frac_bits=0), dict(i0=5, exp_frac_bits=3),
+                                  dict(i0=16, exp_frac_bits=8, intdiv_m=31),
+                                  dict(k_out=4, intdiv_m=20), dict(i0=64, exp_frac_bits=16),
+                                  dict(k_out=2)])
+def test_other_exponent_parameters(torch_dev, over):
+    w = W.make_workload(2, 2, 100, 64, seed=12)
+    check(torch_dev, w, params=dict(w.params, **over), label=f"params {over}")
+    pl = dict(w.params, variant=1, pv_c=28, **over)
+    if pl["intdiv_m"] >= 15:
+        check(torch_dev, w, params=pl, label=f"LIS params {over}")
+
+
+def test_lis_bits(torch_dev):
+    w = W.make_workload(2, 2, 77, 64, seed=13, variant=1)
+    for bits in (1, 2, 3, 4):
+        check(torch_dev, w, params=dict(w.params, lis_bits=bits), label=f"lis_bits={bits}")
+
+
+def test_deterministic_repeat_and_streams(torch_dev):
+    torch = torch_dev
+    from integer_only_quantized_int8_amd.iqattn import IQAttn
+    w = W.make_workload(16, 12, 197, 64, seed=14)
+    att = IQAttn(w.q.shape, w.params)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    torch.cuda.synchronize()
+    att.forward(q, k, v, o1, stream=s1)
+    att.forward(q, k, v, o2, stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    o3 = att.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+    att.close()
+    ref = oracle.forward(w.q, w.k, w.v, w.params, heads=(0, 12))
+    assert np.array_equal(o1.cpu().numpy().reshape(-1, 197, 64)[:12], ref)
+
+
+def test_empty_batch_and_alignment_errors(torch_dev):
+    torch = torch_dev
+    from integer_only_quantized_int8_amd import iqattn as IQ
+    w = W.make_workload(1, 2, 33, 64, seed=15)
+    att = IQ.IQAttn((0, 2, 33, 64), w.params)
+    e = torch.empty((0, 2, 33, 64), dtype=torch.int8, device="cuda:0")
+    att.forward(e, e, e)
+    att.close()
+    att = IQ.IQAttn((1, 2, 33, 64), w.params)
+    buf = torch.zeros(2 * 33 * 64 + 1, dtype=torch.int8, device="cuda:0")
+    mis = buf[1:].view(1, 2, 33, 64)
+    with pytest.raises(IQ.IQAttnError) as ei:
+        att.forward(mis, mis, mis)
+    assert ei.value.code == IQ.IQATTN_E_ALIGN
+    att.close()
