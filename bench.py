@@ -28,12 +28,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
-KERNEL_SRC = os.path.join(ROOT, "integer_only_quantized_int8_amd", "csrc", "iqattn.hip")
+KERNEL_DIR = os.path.join(ROOT, "integer_only_quantized_int8_amd", "csrc")
 METRIC = "integer-only MSA int8 TOPS + % roofline, B=128 H=12 N=197 d=64, 1 MI355X"
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        h.update(name.encode())
+        h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
