@@ -83,13 +83,13 @@ int validate(const iqattn_params* p) {
 bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams* dp) {
   if (p->variant != IQATTN_SHIFTMAX) return false;
   if (!fast_shiftmax_kernel(p->head_dim, kt, p->rel_bias != NULL)) return false;
-  // requantisation: floor(b x / 2^c) = mulhi24(x 2^alpha, b 2^beta), alpha + beta = 32 - c
-  if (p->qk_c > 32 || p->qk_b >= (1 << 23)) return false;
+  // requantisation: floor(b x / 2^c) = mulhi32(x, b << (32 - c)) for
+  // b << (32 - c) < 2^31; padded keys carry mask_s = -(smax + 1), below every
+  // real accumulator; every raw logit then fits the 24-bit v_mad_i32_i24
+  if (p->qk_c > 32 || p->qk_c < 1) return false;
+  if (((int64_t)p->qk_b << (32 - p->qk_c)) >= ((int64_t)1 << 31)) return false;
   const int64_t smax = (int64_t)p->head_dim * 127 * 127 + bias_max;
-  int beta = 32 - p->qk_c;
-  while (beta > 0 && ((int64_t)p->qk_b << beta) >= (1 << 23)) --beta;
-  const int alpha = 32 - p->qk_c - beta;
-  if ((smax << alpha) >= (1 << 23)) return false;
+  if ((((smax + 1) * p->qk_b) >> p->qk_c) >= (1 << 22)) return false;
   // IntDiv: P = floor(e f / 2^sh) = mulhi24(e 2^a, f 2^b), a + b = 32 - sh
   const int64_t e0 = (int64_t)p->i0 << p->exp_frac_bits;
   const int sh = p->intdiv_m - (p->k_out - 1);
@@ -105,15 +105,15 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   if ((e0 << ea) >= (1 << 24)) return false;
   if ((int64_t)kt * 16 * (e0 << ea) >= ((int64_t)1 << 32)) return false;  // row sum
   if ((int64_t)kt * 16 * e0 >= (1 << 24)) return false;                  // float sum
-  dp->alpha = alpha;
-  dp->qk_bm = p->qk_b << beta;
-  dp->mask_s = -(1 << (23 - alpha));
+  dp->qk_bm = (int32_t)((int64_t)p->qk_b << (32 - p->qk_c));
+  dp->mask_s = (int32_t)(-(smax + 1));
   dp->e_shift = ea;
   dp->f_shift = fb;
   dp->e0 = (int32_t)e0;
   dp->e0_pow2 = pow2 ? 1 : 0;
-  dp->pv_fast = (p->pv_c <= 31 && p->pv_b < (1 << 23) &&
-                 ((int64_t)127 << (p->k_out - 1)) * p->pv_b < ((int64_t)1 << 31)) ? 1 : 0;
+  dp->pv_fast = (p->pv_c >= 1 && p->pv_c <= 32 &&
+                 ((int64_t)p->pv_b << (32 - p->pv_c)) < ((int64_t)1 << 31)) ? 1 : 0;
+  dp->pv_bm = dp->pv_fast ? (int32_t)((int64_t)p->pv_b << (32 - p->pv_c)) : 0;
   return true;
 }
 
@@ -201,9 +201,10 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
     const size_t kbytes = (size_t)Np * (D + 16);
     size_t vbytes;
     if (c->fast) {
-      vbytes = (size_t)D * (KS * 64 + 16);
+      const size_t kfast = (size_t)Np * (D == 64 ? 64 : D + 16);
+      vbytes = (size_t)KS * D * 64;
       c->fn = fast_shiftmax_kernel(D, KT, p->rel_bias != NULL);
-      c->lds_bytes = kbytes + vbytes + (size_t)(c->dp.exp_last + 1) * kExpRep * 4;
+      c->lds_bytes = kfast + vbytes + (size_t)(c->dp.exp_last + 1) * kFastExpRep * 4;
     } else {
       vbytes = (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
       c->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);

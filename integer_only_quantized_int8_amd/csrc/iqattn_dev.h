@@ -20,6 +20,7 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kExpRep = 32;  // copies of the exponential table in LDS, one per bank
+constexpr int kFastExpRep = 1;  // table copies in the specialised kernels
 
 struct DevParams {
   const int8_t* q;
@@ -34,10 +35,10 @@ struct DevParams {
   int32_t intdiv_m, p_shift, p_max;
   int32_t lis_f;
   // constants of the fast kernels (see the host's eligibility checks)
-  int32_t alpha, qk_bm, mask_s;  // L_raw = mulhi24(S << alpha, qk_bm); padded keys carry mask_s
+  int32_t qk_bm, mask_s;         // L_raw = mulhi(S, qk_bm); padded keys carry mask_s
   int32_t e_shift, f_shift;      // table holds e << e_shift; F = f_adj << f_shift
   int32_t e0, e0_pow2;           // e(0) and whether it divides 2^M
-  int32_t pv_fast;               // output requantisation fits 32-bit arithmetic
+  int32_t pv_fast, pv_bm;        // output requantisation as mulhi(o, pv_bm)
 };
 
 typedef void (*KernelFn)(DevParams);
@@ -64,30 +65,24 @@ __device__ __forceinline__ uint32_t mulhi_u24(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ int32_t clamp127(int32_t x) { return min(max(x, -127), 127); }
 
-// Raw requantised logit floor((b x) / 2^c) as v_lshlrev + v_mul_hi_i32_i24:
-// x << alpha and bm = b << beta are both signed 24-bit, alpha + beta = 32 - c.
-__device__ __forceinline__ int32_t requant_raw24(int32_t x, int32_t alpha, int32_t bm) {
-  int32_t t;
-  asm("v_lshlrev_b32 %0, %1, %2\n\t"
-      "v_mul_hi_i32_i24 %0, %3, %0"
-      : "=&v"(t)
-      : "s"(alpha), "v"(x), "s"(bm));
-  return t;
+// floor(x * bm / 2^32) = floor((b x) / 2^c) for bm = b << (32 - c) < 2^31:
+// the requantised logit before saturation, one v_mul_hi_i32 (full rate).
+__device__ __forceinline__ int32_t mulhi_i32(int32_t x, int32_t bm) {
+  return (int32_t)(((int64_t)x * (int64_t)bm) >> 32);
 }
 
-// Byte offset of the exponential-table entry for accumulator x of a row whose
-// offset of index 0 is rb: clamp(rb - 128 * L_raw(x), lo, hi), where the clamp
-// is the [-127, 127] saturation of the logit.  Four VALU instructions.
-__device__ __forceinline__ int32_t exp_offset(int32_t x, int32_t alpha, int32_t bm,
-                                              int32_t neg128, int32_t rb, int32_t lo,
-                                              int32_t hi) {
+// Byte address of the exponential-table entry for accumulator x of a row
+// whose entry-0 address is rb: clamp(rb + estr_neg * L_raw(x), lo, hi); the
+// clamp is the [-127, 127] saturation of the logit.  Three VALU instructions
+// (v_mul_hi_i32, v_mad_i32_i24, v_med3_i32).
+__device__ __forceinline__ int32_t exp_offset(int32_t x, int32_t bm, int32_t estr_neg,
+                                              int32_t rb, int32_t lo, int32_t hi) {
   int32_t a;
-  asm("v_lshlrev_b32 %0, %1, %2\n\t"
-      "v_mul_hi_i32_i24 %0, %3, %0\n\t"
-      "v_mad_i32_i24 %0, %0, %4, %5\n\t"
-      "v_med3_i32 %0, %0, %6, %7"
+  asm("v_mul_hi_i32 %0, %1, %2\n\t"
+      "v_mad_i32_i24 %0, %0, %3, %4\n\t"
+      "v_med3_i32 %0, %0, %5, %6"
       : "=&v"(a)
-      : "s"(alpha), "v"(x), "s"(bm), "s"(neg128), "v"(rb), "v"(lo), "v"(hi));
+      : "v"(x), "s"(bm), "s"(estr_neg), "v"(rb), "v"(lo), "v"(hi));
   return a;
 }
 
@@ -125,16 +120,21 @@ __device__ __forceinline__ uint32_t lds_read_u32(uint32_t addr) {
 }
 
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the 16-lane rows of a
+// wave64): v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap pairs
+// the two halves; each lane ends with the reduction of all four.
 __device__ __forceinline__ int32_t wave_max4(int32_t x) {
-  x = max(x, __shfl_xor(x, 16));
-  x = max(x, __shfl_xor(x, 32));
-  return x;
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = max((int32_t)a[0], (int32_t)a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max((int32_t)b[0], (int32_t)b[1]);
 }
 
 __device__ __forceinline__ uint32_t wave_sum4(uint32_t x) {
-  x += (uint32_t)__shfl_xor((int)x, 16);
-  x += (uint32_t)__shfl_xor((int)x, 32);
-  return x;
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] + a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] + b[1];
 }
 
 // low bytes of four values packed little-endian into one word
