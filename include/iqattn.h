@@ -62,6 +62,14 @@ extern "C" {
 #define IQATTN_SHIFTMAX 0
 #define IQATTN_LIS      1
 
+/* P.V engines of the Log-Int-Softmax variant (identical results):
+ * VALU: sum_j V_j << (F - code_j) with one shift-add per (query, key, feature),
+ *       the BitShift operator of FQ-ViT's abstract;
+ * MFMA: the same sum as two int8 matrix products over the bit planes of the
+ *       weights 2^(F - code).                                                  */
+#define IQATTN_LIS_VALU 0
+#define IQATTN_LIS_MFMA 1
+
 #define IQATTN_MAX_SEQ 640       /* largest N of the fused register-resident kernel */
 
 /* Parameters of one attention shape.  All values are plain integers.
@@ -72,8 +80,9 @@ extern "C" {
  *   1 <= qk_b, pv_b <= 2^31 - 1;  0 <= qk_c, pv_c <= 62;
  *   1 <= i0, 0 <= exp_frac_bits, i0 * 2^exp_frac_bits <= 2^22;
  *   2 <= k_out <= 8;  k_out - 1 <= intdiv_m <= 31;
- *   variant IQATTN_SHIFTMAX or IQATTN_LIS; for LIS 1 <= lis_bits <= 4 and
- *   intdiv_m >= 2^lis_bits - 1;
+ *   variant IQATTN_SHIFTMAX or IQATTN_LIS; for LIS 1 <= lis_bits <= 4,
+ *   intdiv_m >= 2^lis_bits - 1 and lis_engine IQATTN_LIS_VALU or
+ *   IQATTN_LIS_MFMA (ignored for Shiftmax);
  *   rel_bias == NULL and window == 0, or rel_bias != NULL, window >= 1,
  *   seq_len == window * window and |rel_bias[.]| <= 2^30.              */
 typedef struct iqattn_params {
@@ -86,6 +95,7 @@ typedef struct iqattn_params {
   int32_t k_out;             /* Shiftmax output bits                            */
   int32_t variant;           /* IQATTN_SHIFTMAX or IQATTN_LIS                   */
   int32_t lis_bits;          /* LIS code bits                                   */
+  int32_t lis_engine;        /* IQATTN_LIS_VALU or IQATTN_LIS_MFMA               */
   int32_t window;            /* w when rel_bias != NULL, else 0                 */
   const int32_t* rel_bias;   /* HOST pointer, [heads][(2w-1)^2] int32, or NULL;
                                 copied by iqattn_create                         */

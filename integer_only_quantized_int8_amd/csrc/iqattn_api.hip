@@ -66,6 +66,7 @@ int validate(const iqattn_params* p) {
   if (p->variant == IQATTN_LIS) {
     if (p->lis_bits < 1 || p->lis_bits > 4) return IQATTN_E_INVAL;
     if (p->intdiv_m < (1 << p->lis_bits) - 1) return IQATTN_E_INVAL;
+    if (p->lis_engine != IQATTN_LIS_VALU && p->lis_engine != IQATTN_LIS_MFMA) return IQATTN_E_INVAL;
   }
   if (p->rel_bias == NULL) {
     if (p->window != 0) return IQATTN_E_INVAL;
@@ -78,11 +79,17 @@ int validate(const iqattn_params* p) {
   return IQATTN_OK;
 }
 
-// Constants of the fast Shiftmax kernel, or false if some step of it would
-// leave its 24/32-bit range for these parameters.
+// Back end of the specialised kernel for these parameters.
+int fast_variant(const iqattn_params* p) {
+  if (p->variant == IQATTN_SHIFTMAX) return kFastShiftmax;
+  return p->lis_engine == IQATTN_LIS_MFMA ? kFastLisMfma : kFastLisValu;
+}
+
+// Constants of the specialised kernel, or false if some step of it would
+// leave its 32-bit range for these parameters (the generic kernel runs then).
 bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams* dp) {
-  if (p->variant != IQATTN_SHIFTMAX) return false;
-  if (!fast_shiftmax_kernel(p->head_dim, kt, p->rel_bias != NULL)) return false;
+  const int var = fast_variant(p);
+  if (!fast_kernel(p->head_dim, kt, p->rel_bias != NULL, var)) return false;
   // requantisation: floor(b x / 2^c) = mulhi32(x, b << (32 - c)) for
   // b << (32 - c) < 2^31; padded keys carry mask_s = -(smax + 1), below every
   // real accumulator; every raw logit then fits the 24-bit v_mad_i32_i24
@@ -90,21 +97,23 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   if (((int64_t)p->qk_b << (32 - p->qk_c)) >= ((int64_t)1 << 31)) return false;
   const int64_t smax = (int64_t)p->head_dim * 127 * 127 + bias_max;
   if ((((smax + 1) * p->qk_b) >> p->qk_c) >= (1 << 22)) return false;
-  // IntDiv: P = floor(e f / 2^sh) = mulhi24(e 2^a, f 2^b), a + b = 32 - sh
+  // IntDiv product: floor(e f / 2^sh) = mulhi32(e 2^ea, f 2^fb), ea + fb = 32 - sh,
+  // sh = M - (k_out - 1) (Shiftmax) or M - F (LIS); the table holds e 2^ea
   const int64_t e0 = (int64_t)p->i0 << p->exp_frac_bits;
-  const int sh = p->intdiv_m - (p->k_out - 1);
-  if (e0 > ((int64_t)1 << sh)) return false;
   const int64_t two_m = (int64_t)1 << p->intdiv_m;
+  const int F = (1 << p->lis_bits) - 1;
+  const int sh = (var == kFastShiftmax) ? p->intdiv_m - (p->k_out - 1) : p->intdiv_m - F;
+  if (sh < 0 || sh > 32 || p->intdiv_m > 30) return false;
+  const int64_t np = (int64_t)kt * 16;
+  if (np * e0 >= (1 << 24)) return false;           // exact float row sum
+  if (two_m / e0 > (1 << 22)) return false;         // reciprocal estimate within 1/2
   const bool pow2 = (e0 & (e0 - 1)) == 0 && e0 <= two_m;
-  const int64_t fmax = pow2 ? two_m / e0 - 1 : two_m / e0;
-  if (fmax >= (1 << 24) || two_m / e0 > (1 << 22) || p->intdiv_m > 30) return false;
+  if (var == kFastShiftmax && e0 > ((int64_t)1 << sh)) return false;  // f - 1 clamp case
   const int tot = 32 - sh;
-  int fb = tot;
-  while (fb > 0 && (fmax << fb) >= (1 << 24)) --fb;
-  const int ea = tot - fb;
-  if ((e0 << ea) >= (1 << 24)) return false;
-  if ((int64_t)kt * 16 * (e0 << ea) >= ((int64_t)1 << 32)) return false;  // row sum
-  if ((int64_t)kt * 16 * e0 >= (1 << 24)) return false;                  // float sum
+  int ea = 0;
+  while (ea < tot && np * (e0 << (ea + 1)) < ((int64_t)1 << 32)) ++ea;  // row sum fits
+  const int fb = tot - ea;
+  if (((two_m / e0) << fb) >= ((int64_t)1 << 32)) return false;
   dp->qk_bm = (int32_t)((int64_t)p->qk_b << (32 - p->qk_c));
   dp->mask_s = (int32_t)(-(smax + 1));
   dp->e_shift = ea;
@@ -128,6 +137,7 @@ struct iqattn_ctx {
   size_t lds_bytes;
   DevParams dp;
   int fast;
+  int grid;
 };
 
 extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
@@ -201,10 +211,12 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
     const size_t kbytes = (size_t)Np * (D + 16);
     size_t vbytes;
     if (c->fast) {
+      const int var = fast_variant(p);
       const size_t kfast = (size_t)Np * (D == 64 ? 64 : D + 16);
-      vbytes = (size_t)KS * D * 64;
-      c->fn = fast_shiftmax_kernel(D, KT, p->rel_bias != NULL);
-      c->lds_bytes = kfast + vbytes + (size_t)(c->dp.exp_last + 1) * kFastExpRep * 4;
+      vbytes = (var == kFastLisValu) ? (size_t)Np * D : (size_t)KS * D * 64;
+      c->fn = fast_kernel(D, KT, p->rel_bias != NULL, var);
+      c->lds_bytes = kfast + vbytes + (((size_t)(c->dp.exp_last + 1) * 4 + 15) & ~(size_t)15) +
+                     (var == kFastLisValu ? (size_t)kWaves * 256 * 4 : 0);
     } else {
       vbytes = (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
       c->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);
@@ -228,6 +240,22 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   c->dp.heads = p->heads;
   c->dp.n = N;
   c->dp.units = p->batch * p->heads;
+  c->dp.n_full = c->dp.units;
+  c->grid = c->dp.units;
+  if (c->fast && c->dp.units > 0) {
+    // heads of a last, partial round of blocks are split into quarter heads
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)c->fn, kThreads,
+                                                     c->lds_bytes) == hipSuccess &&
+        per_cu > 0) {
+      const int64_t slots = (int64_t)per_cu * prop.multiProcessorCount;
+      const int64_t rem = c->dp.units % slots;
+      if (rem > 0 && rem * 2 <= slots) {
+        c->dp.n_full = (int32_t)(c->dp.units - rem);
+        c->grid = (int)(c->dp.n_full + ((rem + 7) / 8) * 32);
+      }
+    }
+  }
   c->dp.qk_b = p->qk_b;
   c->dp.qk_c = p->qk_c;
   c->dp.pv_b = p->pv_b;
@@ -257,7 +285,7 @@ extern "C" int iqattn_forward(iqattn_ctx* c, const int8_t* q, const int8_t* k, c
   dp.k = k;
   dp.v = v;
   dp.out = out;
-  hipLaunchKernelGGL(c->fn, dim3(dp.units), dim3(kThreads), c->lds_bytes,
+  hipLaunchKernelGGL(c->fn, dim3(c->grid), dim3(kThreads), c->lds_bytes,
                      (hipStream_t)hip_stream, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqattn launch");

@@ -19,8 +19,12 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kExpRep = 32;  // copies of the exponential table in LDS, one per bank
-constexpr int kFastExpRep = 1;  // table copies in the specialised kernels
+constexpr int kExpRep = 32;  // copies of the exponential table in LDS (generic kernel)
+
+// back ends of the specialised kernels
+constexpr int kFastShiftmax = 0;
+constexpr int kFastLisValu = 1;
+constexpr int kFastLisMfma = 2;
 
 struct DevParams {
   const int8_t* q;
@@ -30,6 +34,7 @@ struct DevParams {
   const uint32_t* exp_tab;   // [256] e(-idx), or e(-idx) << e_shift for the fast kernels
   const int32_t* bias;       // [heads][Np][Np] expanded, query-major, or null
   int32_t heads, n, units;
+  int32_t n_full;            // blocks [0, n_full) take whole heads, later blocks quarter heads
   int32_t qk_b, qk_c, pv_b, pv_c;
   int32_t exp_last;          // first table index whose entry is 0 (or 255)
   int32_t intdiv_m, p_shift, p_max;
@@ -51,16 +56,10 @@ __device__ __forceinline__ int32_t requant_i8(int32_t x, int32_t b, int32_t c) {
   return (int32_t)y;
 }
 
-// floor(a * b / 2^32) for a, b in signed 24-bit range: v_mul_hi_i32_i24.
-__device__ __forceinline__ int32_t mulhi_i24(int32_t a, int32_t b) {
-  return (int32_t)(((int64_t)__builtin_amdgcn_sbfe(a, 0, 24) *
-                    (int64_t)__builtin_amdgcn_sbfe(b, 0, 24)) >> 32);
-}
 
-// floor(a * b / 2^32) for a, b in unsigned 24-bit range: v_mul_hi_u32_u24.
-__device__ __forceinline__ uint32_t mulhi_u24(uint32_t a, uint32_t b) {
-  return (uint32_t)(((uint64_t)__builtin_amdgcn_ubfe(a, 0, 24) *
-                     (uint64_t)__builtin_amdgcn_ubfe(b, 0, 24)) >> 32);
+// floor(a * b / 2^32) for unsigned 32-bit a, b: v_mul_hi_u32 (full rate).
+__device__ __forceinline__ uint32_t mulhi_u32(uint32_t a, uint32_t b) {
+  return (uint32_t)(((uint64_t)a * (uint64_t)b) >> 32);
 }
 
 __device__ __forceinline__ int32_t clamp127(int32_t x) { return min(max(x, -127), 127); }
@@ -86,18 +85,18 @@ __device__ __forceinline__ int32_t exp_offset(int32_t x, int32_t bm, int32_t est
   return a;
 }
 
-// Four Shiftmax probabilities P = (e f) >> (M - k_out + 1) = mulhi24(e 2^a, f 2^b)
+// Four Shiftmax probabilities P = (e f) >> (M - k_out + 1) = mulhi(e 2^a, f 2^b)
 // packed little-endian into one int8 word of the P.V MFMA operand.  The asm
 // block makes the two 16-bit halves; the final merge is a compiler-visible
 // v_perm so that the MFMA hazard checks see the instruction that feeds it.
 __device__ __forceinline__ uint32_t p4_pack(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3,
                                             uint32_t F) {
   uint32_t lo, hi, t;
-  asm("v_mul_hi_u32_u24 %0, %3, %7\n\t"
-      "v_mul_hi_u32_u24 %2, %4, %7\n\t"
+  asm("v_mul_hi_u32 %0, %3, %7\n\t"
+      "v_mul_hi_u32 %2, %4, %7\n\t"
       "v_lshl_or_b32 %0, %2, 8, %0\n\t"
-      "v_mul_hi_u32_u24 %1, %5, %7\n\t"
-      "v_mul_hi_u32_u24 %2, %6, %7\n\t"
+      "v_mul_hi_u32 %1, %5, %7\n\t"
+      "v_mul_hi_u32 %2, %6, %7\n\t"
       "v_lshl_or_b32 %1, %2, 8, %1"
       : "=&v"(lo), "=&v"(hi), "=&v"(t)
       : "v"(e0), "v"(e1), "v"(e2), "v"(e3), "v"(F));
@@ -189,6 +188,6 @@ __device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
 
 // host-side selectors, one per translation unit
 KernelFn generic_kernel(int d, int ktm, int variant, bool bias);
-KernelFn fast_shiftmax_kernel(int d, int kt, bool bias);  // null if not instantiated
+KernelFn fast_kernel(int d, int kt, bool bias, int var);  // null if not instantiated
 
 }  // namespace iqattn

@@ -27,6 +27,8 @@ IQATTN_E_ALIGN = -6
 IQATTN_E_DEVICE = -7
 IQATTN_SHIFTMAX = 0
 IQATTN_LIS = 1
+IQATTN_LIS_VALU = 0
+IQATTN_LIS_MFMA = 1
 IQATTN_MAX_SEQ = 640
 
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror")
@@ -35,7 +37,7 @@ EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerro
 class iqattn_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "heads", "seq_len", "head_dim", "qk_b", "qk_c", "pv_b", "pv_c", "i0",
-        "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "window")] + \
+        "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "lis_engine", "window")] + \
         [("rel_bias", C.POINTER(C.c_int32))]
 
 
@@ -76,7 +78,7 @@ def make_params(shape, params: Dict[str, object]):
     p = iqattn_params()
     p.batch, p.heads, p.seq_len, p.head_dim = int(B), int(H), int(N), int(d)
     for name in ("qk_b", "qk_c", "pv_b", "pv_c", "i0", "exp_frac_bits", "intdiv_m", "k_out",
-                 "variant", "lis_bits", "window"):
+                 "variant", "lis_bits", "lis_engine", "window"):
         setattr(p, name, int(params.get(name, 0) or 0))
     keep = None
     rb = params.get("rel_bias")

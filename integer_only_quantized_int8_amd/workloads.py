@@ -130,7 +130,7 @@ def default_params(seed: int, variant: int = SHIFTMAX) -> Dict[str, object]:
     return dict(qk_b=int(b[0]), qk_c=22, pv_b=int(b[1]),
                 pv_c=28 if variant == LIS else 20,
                 i0=16, exp_frac_bits=8, intdiv_m=30, k_out=8,
-                variant=variant, lis_bits=4, window=0, rel_bias=None)
+                variant=variant, lis_bits=4, lis_engine=0, window=0, rel_bias=None)
 
 
 def make_workload(batch: int, heads: int, seq_len: int, head_dim: int, seed: int,

@@ -42,7 +42,8 @@ def test_header_constants_match_binding():
     text = open(os.path.join(ROOT, "include", "iqattn.h")).read()
     for name in ("IQATTN_OK", "IQATTN_E_INVAL", "IQATTN_E_SHAPE", "IQATTN_E_ALLOC",
                  "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
-                 "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_MAX_SEQ"):
+                 "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_LIS_VALU", "IQATTN_LIS_MFMA",
+                 "IQATTN_MAX_SEQ"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(IQ, name), name
 
@@ -72,6 +73,8 @@ def _create_rc(lib, shape, **over):
     ((1, 1, 16, 64), {"variant": 2}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"variant": 1, "lis_bits": 5}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"variant": 1, "intdiv_m": 14}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"variant": 1, "lis_engine": 2}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"variant": 1, "lis_engine": -1}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"window": 4}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"window": 3, "rel_bias": np.zeros((1, 25), np.int32)}, IQ.IQATTN_E_SHAPE),
     ((1, 1, 16, 64), {"window": 4, "rel_bias": np.full((1, 49), (1 << 30) + 1, np.int32)},

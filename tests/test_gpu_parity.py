@@ -44,24 +44,34 @@ def run_gpu(torch, w, params=None, stream=None):
 
 
 def check(torch, w, params=None, heads=None, label=""):
+    """Compare the GPU output with the oracle.  A Log-Int-Softmax case runs both
+    P.V engines (VALU shift-add and MFMA bit planes) against the same oracle
+    result."""
     params = w.params if params is None else params
-    _say(f"[parity] {label} {w.q.shape} variant={params['variant']} heads={heads}")
-    got = run_gpu(torch, w, params)
+    engines = [0, 1] if params["variant"] == 1 else [None]
     total = w.batch * w.heads
     N, d = w.seq_len, w.head_dim
-    got = got.reshape(total, N, d)
+    gots = []
+    for eng in engines:
+        pe = params if eng is None else dict(params, lis_engine=eng)
+        _say(f"[parity] {label} {w.q.shape} variant={params['variant']} engine={eng} "
+             f"heads={heads}")
+        gots.append((eng, run_gpu(torch, w, pe).reshape(total, N, d)))
     if heads is None:
-        sel = np.arange(total)
         ref = oracle.forward(w.q, w.k, w.v, params)
-        assert np.array_equal(got, ref), f"{label}: mismatch"
+        for eng, got in gots:
+            if not np.array_equal(got, ref):
+                bad = np.argwhere(got != ref)
+                raise AssertionError(f"{label} engine={eng}: {len(bad)} entries differ, "
+                                     f"first {bad[:4].tolist()}")
         return
-    sel = heads
-    for u in sel:
+    for u in heads:
         ref = oracle.forward(w.q, w.k, w.v, params, heads=(int(u), int(u) + 1))[0]
-        if not np.array_equal(got[u], ref):
-            bad = np.argwhere(got[u] != ref)
-            raise AssertionError(f"{label}: head {u} differs at {len(bad)} entries, "
-                                 f"first {bad[:4].tolist()}")
+        for eng, got in gots:
+            if not np.array_equal(got[u], ref):
+                bad = np.argwhere(got[u] != ref)
+                raise AssertionError(f"{label} engine={eng}: head {u} differs at {len(bad)} "
+                                     f"entries, first {bad[:4].tolist()}")
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 3])
