@@ -12,6 +12,12 @@ resident in HBM).  Prints one JSON line:
   traffic    HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE,
              read from profiles/ when recorded for the current kernel source
   cpu_baseline  the CPU oracle (single thread) on the same inputs
+
+`--record-traffic FETCH_CSV WRITE_CSV` turns the counter files of two
+rocprofv3 --pmc runs of `bench.py --copy-calib` (FETCH_SIZE, then WRITE_SIZE)
+into profiles/traffic_<workload>.json: each counter's KiB per dispatch of the
+attention kernel, scaled by the factor that maps the same counter on the
+256 MiB device copy to its known size.
 """
 from __future__ import annotations
 
@@ -50,6 +56,42 @@ def load_traffic(workload: str):
     return rec
 
 
+COPY_CALIB_BYTES = 256 << 20
+
+
+def _counter_rows(path, counter):
+    import csv
+    return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+
+def _is_attention_kernel(name: str) -> bool:
+    return "iqattn::" in name and ("iqattn_fast" in name or "iqattn_generic" in name)
+
+
+def record_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
+    """Calibrated HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch)."""
+    rec = {"workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+           "copy_calibration_bytes": COPY_CALIB_BYTES}
+    total = 0.0
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                               ("write", write_csv, "WRITE_SIZE")):
+        rows = _counter_rows(path, counter)
+        kern = [float(r["Counter_Value"]) for r in rows if _is_attention_kernel(r["Kernel_Name"])]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] or "elementwise" in r["Kernel_Name"]]
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no attention-kernel or copy dispatches with {counter}")
+        copy_kib = max(copy)            # the 256 MiB calibration copy is the largest
+        scale = COPY_CALIB_BYTES / (copy_kib * 1024.0)
+        kib = sum(kern) / len(kern)
+        rec[key] = {"counter": counter, "kernel_kib_per_dispatch": round(kib, 3),
+                    "dispatches": len(kern), "copy_kib": round(copy_kib, 3),
+                    "scale": round(scale, 4), "bytes_per_launch": round(kib * 1024.0 * scale)}
+        total += kib * 1024.0 * scale
+    rec["hbm_bytes_per_launch"] = round(total)
+    return rec
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -71,7 +113,22 @@ def main():
                     help="heads timed on the CPU oracle (0 = all heads, at most ~30 s)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "counter files and exit (no GPU use)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        from integer_only_quantized_int8_amd import workloads as W
+        name = W.CONFIGS[args.config]["name"]
+        rec = record_traffic(args.record_traffic[0], args.record_traffic[1], name)
+        out = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -134,7 +191,7 @@ def main():
     del graph
 
     if args.copy_calib:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
@@ -186,20 +243,26 @@ def main():
         import oracle
         if not os.path.exists(oracle.library_path()):
             oracle.build()
-        per_head_guess = 0.006 * (N / 197.0) ** 2 * (d / 64.0)
-        n_cpu = args.cpu_heads or min(heads, max(1, int(30.0 / per_head_guess)))
+        # bounded sample: whole passes over the first n_cpu heads until at least
+        # ~10 s of single-threaded oracle time (at most ~30 s)
+        per_head_guess = 0.0025 * (N / 197.0) ** 2 * (d / 64.0)
+        n_cpu = args.cpu_heads or min(heads, max(1, int(25.0 / per_head_guess)))
         print(f"[bench] CPU oracle on {n_cpu} heads ...", file=sys.stderr, flush=True)
-        t1 = time.perf_counter()
-        ref = oracle.forward(w.q, w.k, w.v, w.params, heads=(0, n_cpu))
-        cpu_s = time.perf_counter() - t1
-        same = bool(np.array_equal(gpu_out.reshape(heads, N, d)[:n_cpu], ref))
+        passes, cpu_s, same = 0, 0.0, True
+        while passes == 0 or (cpu_s < 10.0 and cpu_s * (passes + 1) / passes < 30.0):
+            t1 = time.perf_counter()
+            ref = oracle.forward(w.q, w.k, w.v, w.params, heads=(0, n_cpu))
+            cpu_s += time.perf_counter() - t1
+            passes += 1
+            same = same and bool(np.array_equal(gpu_out.reshape(heads, N, d)[:n_cpu], ref))
+        done = n_cpu * passes
         result["cpu_baseline"] = {
-            "value": round(4.0 * N * N * d * n_cpu / cpu_s / 1e12, 6), "unit": "TOPS",
+            "value": round(4.0 * N * N * d * done / cpu_s / 1e12, 6), "unit": "TOPS",
             "cores": 1, "kind": "oracle",
-            "sample": f"heads 0..{n_cpu - 1} of {w.name} (seed {1000 + args.config}), "
-                      f"{cpu_s:.2f} s single-threaded C -O2 on {cpu_model()} "
-                      f"(host nproc {os.cpu_count()})",
-            "heads_per_s": round(n_cpu / cpu_s, 2)}
+            "sample": f"{passes} pass(es) over heads 0..{n_cpu - 1} of {w.name} "
+                      f"(seed {1000 + args.config}), {cpu_s:.2f} s single-threaded C -O2 on "
+                      f"{cpu_model()} (host nproc {os.cpu_count()})",
+            "heads_per_s": round(done / cpu_s, 2)}
         result["bit_exact_vs_oracle"] = {"heads_compared": n_cpu, "equal": same}
     att.close()
     print(json.dumps(result), flush=True)
