@@ -110,14 +110,32 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   const bool pow2 = (e0 & (e0 - 1)) == 0 && e0 <= two_m;
   if (var == kFastShiftmax && e0 > ((int64_t)1 << sh)) return false;  // f - 1 clamp case
   const int tot = 32 - sh;
-  int ea = 0;
-  while (ea < tot && np * (e0 << (ea + 1)) < ((int64_t)1 << 32)) ++ea;  // row sum fits
-  const int fb = tot - ea;
-  if (((two_m / e0) << fb) >= ((int64_t)1 << 32)) return false;
+  const int64_t fmax = two_m / e0;
+  int ea = 0, fb = 0;
+  bool u24 = false;
+  if (var == kFastShiftmax) {
+    // 24-bit operands (p4_pack24): the largest e shift that keeps e0 << ea and
+    // the row sum in range, if f << fb then fits 24 bits as well
+    for (int a = tot; a >= 0; --a) {
+      const int b = tot - a;
+      if ((e0 << a) < (1 << 24) && np * (e0 << a) < ((int64_t)1 << 32) && (fmax << b) < (1 << 24)) {
+        ea = a;
+        fb = b;
+        u24 = true;
+        break;
+      }
+    }
+  }
+  if (!u24) {
+    while (ea < tot && np * (e0 << (ea + 1)) < ((int64_t)1 << 32)) ++ea;  // row sum fits
+    fb = tot - ea;
+    if ((fmax << fb) >= ((int64_t)1 << 32)) return false;
+  }
   dp->qk_bm = (int32_t)((int64_t)p->qk_b << (32 - p->qk_c));
   dp->mask_s = (int32_t)(-(smax + 1));
   dp->e_shift = ea;
   dp->f_shift = fb;
+  dp->p_u24 = u24 ? 1 : 0;
   dp->e0 = (int32_t)e0;
   dp->e0_pow2 = pow2 ? 1 : 0;
   dp->pv_fast = (p->pv_c >= 1 && p->pv_c <= 32 &&
@@ -138,6 +156,7 @@ struct iqattn_ctx {
   DevParams dp;
   int fast;
   int grid;
+  int block;  // threads per workgroup
 };
 
 extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
@@ -211,15 +230,23 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
     const size_t kbytes = (size_t)Np * (D + 16);
     size_t vbytes;
     if (c->fast) {
+      // buffers (V, K regions of R bytes each), table, LIS shift scratch; the
+      // last V region's operand reads reach KS * 64 rows past its start
       const int var = fast_variant(p);
-      const size_t kfast = (size_t)Np * (D == 64 ? 64 : D + 16);
-      vbytes = (var == kFastLisValu) ? (size_t)Np * D : (size_t)KS * D * 64;
-      c->fn = fast_kernel(D, KT, p->rel_bias != NULL, var);
-      c->lds_bytes = kfast + vbytes + (((size_t)(c->dp.exp_last + 1) * 4 + 15) & ~(size_t)15) +
-                     (var == kFastLisValu ? (size_t)kWaves * 256 * 4 : 0);
+      const bool bias = p->rel_bias != NULL;
+      const size_t R = (size_t)fast_region_bytes(D, KT);
+      const size_t nbuf = (size_t)fast_nbuf(KT, bias);
+      const size_t cw = (size_t)fast_cw(KT, bias);
+      const size_t bs = (size_t)fast_nreg(KT, bias) * R;  // bytes per buffer
+      const size_t used = nbuf * bs + kFastTableBytes + (var == kFastLisValu ? cw * 1024 : 0) + 64;
+      const size_t reach = (nbuf - 1) * bs + (size_t)KS * 64 * D;
+      c->fn = fast_kernel(D, KT, bias, var);
+      c->lds_bytes = used > reach ? used : reach;
+      c->block = (int)(64 * (cw + 1));
     } else {
       vbytes = (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
       c->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);
+      c->block = kThreads;
       c->lds_bytes = kbytes + ((vbytes + 15) & ~(size_t)15) +
                      (size_t)(c->dp.exp_last + 1) * kExpRep * 4 +
                      (p->variant == IQATTN_LIS ? (size_t)kWaves * 256 * 4 : 0);
@@ -241,20 +268,24 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   c->dp.n = N;
   c->dp.units = p->batch * p->heads;
   c->dp.n_full = c->dp.units;
+  c->dp.n_items = c->dp.units;
   c->grid = c->dp.units;
   if (c->fast && c->dp.units > 0) {
-    // heads of a last, partial round of blocks are split into quarter heads
+    // persistent grid: one workgroup per slot the chip holds at once, walking
+    // the work items; the heads of a last, partial round are split into
+    // quarter heads (groups of 8 heads x 4 quarters)
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)c->fn, kThreads,
-                                                     c->lds_bytes) == hipSuccess &&
-        per_cu > 0) {
-      const int64_t slots = (int64_t)per_cu * prop.multiProcessorCount;
-      const int64_t rem = c->dp.units % slots;
-      if (rem > 0 && rem * 2 <= slots) {
-        c->dp.n_full = (int32_t)(c->dp.units - rem);
-        c->grid = (int)(c->dp.n_full + ((rem + 7) / 8) * 32);
-      }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)c->fn, c->block,
+                                                     c->lds_bytes) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    const int64_t slots = (int64_t)per_cu * prop.multiProcessorCount;
+    const int64_t rem = c->dp.units % slots;
+    if (rem > 0 && rem * 2 <= slots) {
+      c->dp.n_full = (int32_t)(c->dp.units - rem);
+      c->dp.n_items = (int32_t)(c->dp.n_full + ((rem + 7) / 8) * 32);
     }
+    c->grid = (int)(c->dp.n_items < slots ? c->dp.n_items : slots);
   }
   c->dp.qk_b = p->qk_b;
   c->dp.qk_c = p->qk_c;
@@ -285,7 +316,7 @@ extern "C" int iqattn_forward(iqattn_ctx* c, const int8_t* q, const int8_t* k, c
   dp.k = k;
   dp.v = v;
   dp.out = out;
-  hipLaunchKernelGGL(c->fn, dim3(c->grid), dim3(kThreads), c->lds_bytes,
+  hipLaunchKernelGGL(c->fn, dim3(c->grid), dim3(c->block), c->lds_bytes,
                      (hipStream_t)hip_stream, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqattn launch");

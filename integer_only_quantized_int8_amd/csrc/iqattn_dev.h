@@ -34,7 +34,8 @@ struct DevParams {
   const uint32_t* exp_tab;   // [256] e(-idx), or e(-idx) << e_shift for the fast kernels
   const int32_t* bias;       // [heads][Np][Np] expanded, query-major, or null
   int32_t heads, n, units;
-  int32_t n_full;            // blocks [0, n_full) take whole heads, later blocks quarter heads
+  int32_t n_full;            // work items [0, n_full) are whole heads, later items quarter heads
+  int32_t n_items;           // whole heads plus quarter-head items (fast kernels)
   int32_t qk_b, qk_c, pv_b, pv_c;
   int32_t exp_last;          // first table index whose entry is 0 (or 255)
   int32_t intdiv_m, p_shift, p_max;
@@ -44,6 +45,7 @@ struct DevParams {
   int32_t e_shift, f_shift;      // table holds e << e_shift; F = f_adj << f_shift
   int32_t e0, e0_pow2;           // e(0) and whether it divides 2^M
   int32_t pv_fast, pv_bm;        // output requantisation as mulhi(o, pv_bm)
+  int32_t p_u24;                 // Shiftmax: e << e_shift and F below 2^24 (p16_pack24)
 };
 
 typedef void (*KernelFn)(DevParams);
@@ -103,11 +105,85 @@ __device__ __forceinline__ uint32_t p4_pack(uint32_t e0, uint32_t e1, uint32_t e
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
+// Sixteen Shiftmax probabilities (four operand words) with e << a and f << b
+// below 2^24: v_mul_hi_u32_u24 returns bits 32..47 of the 48-bit product, and
+// its SDWA form writes the low byte of that result (P < 2^7) straight into byte
+// k of a word, so a word costs four instructions.  A byte write that keeps the
+// other bytes reads the old word without an interlock against the previous
+// write, so the sixteen writes go byte-major: writes to one word are four
+// instructions apart.  The closing s_nop gives the MFMA that reads the words
+// the wait states a VALU write needs, which the compiler cannot insert for an
+// asm block.
+__device__ __forceinline__ void p16_pack24(const v4i& e0, const v4i& e1, const v4i& e2,
+                                           const v4i& e3, uint32_t F, v4i& w) {
+  uint32_t w0, w1, w2, w3;
+  asm(
+      "v_mul_hi_u32_u24_sdwa %0, %4, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %1, %8, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %2, %12, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %3, %16, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %0, %5, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %1, %9, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %2, %13, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %3, %17, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %0, %6, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %1, %10, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %2, %14, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %3, %18, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %0, %7, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %1, %11, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %2, %15, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_u32_u24_sdwa %3, %19, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "s_nop 4"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+      : "v"(e0[0]), "v"(e0[1]), "v"(e0[2]), "v"(e0[3]), "v"(e1[0]), "v"(e1[1]), "v"(e1[2]),
+        "v"(e1[3]), "v"(e2[0]), "v"(e2[1]), "v"(e2[2]), "v"(e2[3]), "v"(e3[0]), "v"(e3[1]),
+        "v"(e3[2]), "v"(e3[3]), "v"(F));
+  w = v4i{(int32_t)w0, (int32_t)w1, (int32_t)w2, (int32_t)w3};
+}
+
 // Inline asm never reads an MFMA result first: the compiler's hazard checks do
 // not look inside asm blocks, so the first reader of every accumulator is
 // ordinary code (which gets the required wait states).
 
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef int32_t v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) uint32_t lds_u32w;
+
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes at rsrc.base + voffset go to
+// LDS at (lds + 16 * lane); offsets at or past rsrc.num_records read as zero.
+__device__ void raw_buffer_load_lds(v4i rsrc, lds_u32w* lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// buffer resource (typed) of a byte range [base, base + bytes): raw access;
+// accesses through it take a 32-bit per-lane offset and the base in SGPRs
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// operand-sized loads through a buffer resource
+template <typename Op>
+__device__ __forceinline__ Op buf_load(__amdgpu_buffer_rsrc_t r, int off);
+template <>
+__device__ __forceinline__ v4i buf_load<v4i>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ int64_t buf_load<int64_t>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// buffer resource of a byte range [base, base + bytes): stride 0, raw access
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  v4i r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)(uint32_t)(a >> 32);
+  r[2] = (int32_t)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
 
 // 32-bit LDS address of a pointer into dynamic shared memory
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -143,6 +219,26 @@ __device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t b0, uint32_t b1, uin
   uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
+
+// ---------------------------------------------------------------- fast-kernel LDS plan
+// K and V of one head occupy one region each, a whole number of 1 KB direct
+// global->LDS blocks (rows beyond N arrive as zeros).  Two buffers (V0 K0 V1 K1)
+// let the next head's loads run under the current head's compute; the
+// exponential table and the LIS shift scratch follow.
+constexpr int fast_region_bytes(int d, int kt) { return ((kt * 16 * d + 1023) / 1024) * 1024; }
+// Rows of up to 256 keys without a bias table run one workgroup per CU: 15
+// compute waves and one loader wave over three (V, K, Q) buffers, so that the
+// waves of a CU share one tile queue (two workgroups on a CU drift apart: the
+// older one's waves win the issue arbitration and the younger one finishes
+// alone).  Longer rows (about 250 VGPRs per lane) and bias-table rows use
+// 3 compute waves, one (V, K) buffer, and several workgroups per CU.
+constexpr bool fast_big(int kt, bool bias) { return !bias && kt <= 16; }
+constexpr int fast_nbuf(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 1; }
+constexpr int fast_nreg(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 2; }
+constexpr int fast_cw(int kt, bool bias) { return fast_big(kt, bias) ? 15 : 3; }
+// minimum waves per SIMD the register allocation must allow
+constexpr int fast_waves_per_eu(int kt, bool bias) { return fast_big(kt, bias) ? 4 : 2; }
+constexpr int kFastTableBytes = 1024;  // LDS copy of the 256-entry table
 
 // position of key kappa inside its 64-key block of the staged V^T rows:
 // key 16*tt + 4*g + r sits at byte 16*g + 4*tt + r, so that the P.V MFMA's

@@ -2,6 +2,12 @@
 // 16-key tiles (KT, so N in (16(KT-1), 16 KT]) for the parameter ranges in
 // which every step fits 32-bit VALU arithmetic (the host checks them).
 //
+// Work distribution: a persistent grid (as many workgroups as fit on the chip)
+// walks a list of work items -- whole heads, then the heads of a last partial
+// round split into quarter heads.  K and V of a head reach LDS through direct
+// global->LDS loads (buffer_load ... lds, no registers); with two buffers the
+// next item's loads run while the current item is computed.
+//
 // Front end, per 16-query tile of a wave (shared by every variant):
 //   S^T = K . Q^T   one int8 MFMA per 16-key tile, accumulators in VGPRs;
 //   pass 1          row max (plain max: the first reads of MFMA results);
@@ -20,13 +26,13 @@
 //                   o = -(O_0 + 256 O_1).
 // Padded keys (j >= N) get the accumulator init mask_s below every real
 // accumulator, so they never win the row max; their table entry is removed
-// from the row sum once per lane, and their V rows are zero in LDS.
+// from the row sum once per lane, and their K and V rows are zero in LDS.
 //
-// LDS layout (no padding): K as 64-byte rows (d = 64) whose four 16-byte
-// chunks are XOR-swizzled by (row >> 1) & 3, which makes the b128 operand
-// reads of 16 rows x 4 chunks bank-conflict free on gfx950 (d = 32 keeps
-// 48-byte padded rows); V^T as [64-key step][feature][64 bytes] with the same
-// swizzle (V row-major for the VALU LIS back end); one exponential table.
+// LDS: V and K as row-major regions of whole 1 KB load blocks, 16-byte chunks
+// XOR-swizzled per row so that the MFMA operand reads are bank-conflict free;
+// the V^T operand of P.V comes from ds_read_b64_tr_b8 (8 keys x 16 features
+// per 16-lane group), so V needs no transpose on the way in.  One exponential
+// table per workgroup.
 //
 // Method passages: I-ViT (mer.run summary) sec. 3.2 "Dyadic Arithmetic for
 // Linear Operations" and sec. 3.3 "Integer-only Softmax: Shiftmax"; FQ-ViT
@@ -38,8 +44,18 @@
 namespace iqattn {
 namespace {
 
-// byte offset of 16-byte chunk `c` of 64-byte row `r` after the XOR swizzle
-__device__ __forceinline__ int swz64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
+// XOR swizzles of the 16-byte chunk index of an LDS row.  K (b128 / b64
+// operand reads of 16 rows): d = 64 by (row >> 1) & 3, d = 32 by (row >> 3) & 1.
+// V (transpose reads of keys 16 tt + 4 g + r): d = 64 by bits 2 and 4 of the
+// key, d = 32 by bit 4; both spread a half-wave over distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 64 ? (row >> 1) & 3 : (row >> 3) & 1;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 64 ? (((row >> 2) & 1) | ((row >> 3) & 2)) : (row >> 4) & 1;
+}
 
 // LIS shift w = F - code for the probability Ph (Ph < 2^24):
 // code = F - ilog2r(Ph) clipped to [0, F], Ph = 0 -> code F.  ilog2r(x) is the
@@ -64,109 +80,176 @@ __device__ __forceinline__ void lis_planes(const v4i& w, int32_t& lo, int32_t& h
   hi = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
 }
 
+// One work item: head u (-1 past the end) and its query tiles qt0, qt0 + qstep,
+// ... (T of them).  Whole heads take every tile; a head of the last partial
+// round is split into four quarter items (tiles q, q + 4, ...).  The quarters
+// of a head sit 8 items apart, so with a grid that is a multiple of 8 they run
+// on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2
+// for the K/V reads.
+struct Item {
+  int u, qt0, qstep, T;
+};
+
+template <int KT>
+__device__ __forceinline__ Item decode_item(const DevParams& p, int k) {
+  Item it;
+  it.u = -1;
+  it.qt0 = 0;
+  it.qstep = 1;
+  it.T = 0;
+  if (k >= p.n_items) return it;
+  if (k < p.n_full) {
+    it.u = k;
+    it.T = KT;
+  } else {
+    const int r = k - p.n_full, kk = r >> 3, q = kk & 3;
+    const int u = p.n_full + (kk >> 2) * 8 + (r & 7);
+    if (u < p.units) it.u = u;
+    it.qt0 = q;
+    it.qstep = 4;
+    it.T = q < KT ? (KT - q + 3) / 4 : 0;
+  }
+  return it;
+}
+
+// Direct loads of head u's V, K (and Q) (R / 1024 blocks each) into the LDS
+// regions at vbuf, vbuf + R (and vbuf + 2R), issued by one wave.  Lane l of block i fills LDS bytes
+// [1024 i + 16 l, +16) = (row, chunk position cp) from source chunk
+// cp ^ swizzle(row).  Rows >= N lie past the buffer range and arrive as zeros.
+template <int D, int R, bool WITH_Q>
+__device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t vbuf, int lane) {
+  constexpr int NB = R / 1024;
+  const int64_t hb = (int64_t)u * p.n * D;
+  const uint32_t bytes = (uint32_t)(p.n * D);
+  const v4i rk = make_rsrc(p.k + hb, bytes);
+  const v4i rv = make_rsrc(p.v + hb, bytes);
+  const v4i rq = make_rsrc(p.q + hb, bytes);
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int o = blk * 1024 + 16 * lane;
+    const int row = o / D, cp = (o % D) >> 4;
+    const int ko = row * D + 16 * (cp ^ kswz<D>(row));
+    raw_buffer_load_lds(rv, (lds_u32w*)(uintptr_t)(vbuf + blk * 1024), 16,
+                        row * D + 16 * (cp ^ vswz<D>(row)), 0, 0, 0);
+    raw_buffer_load_lds(rk, (lds_u32w*)(uintptr_t)(vbuf + R + blk * 1024), 16, ko, 0, 0, 0);
+    if (WITH_Q)
+      raw_buffer_load_lds(rq, (lds_u32w*)(uintptr_t)(vbuf + 2 * R + blk * 1024), 16, ko, 0, 0, 0);
+  }
+}
+
+// V^T operands of one 64-key step (FT 16-feature tiles) by transpose reads:
+// two ds_read_b64_tr_b8 per tile at the lane offsets vtr[0], vtr[1], the
+// feature tile entering as an XOR of the 16-byte chunk index.
+template <int D, int FT>
+__device__ __forceinline__ void read_vt(uint32_t vb, const int (&vtr)[2], v4i (&vop)[FT]) {
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(vb + (vtr[0] ^ (ft << 4))));
+    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(vb + (vtr[1] ^ (ft << 4))));
+    vop[ft] = v4i{r0[0], r0[1], r1[0], r1[1]};
+  }
+}
+
+// Output requantisation and store of a lane's 4 x FT int32 sums (features
+// 16 ft + 4 g + r of one query, at byte offset dst + 16 ft of the head).
+template <int FT>
+__device__ __forceinline__ void store_out(const DevParams& p, const v4i (&O)[FT],
+                                          __amdgpu_buffer_rsrc_t ores, int dst) {
+  if (p.pv_fast) {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          pack4_lowbytes((uint32_t)clamp127(mulhi_i32(O[ft][0], p.pv_bm)),
+                         (uint32_t)clamp127(mulhi_i32(O[ft][1], p.pv_bm)),
+                         (uint32_t)clamp127(mulhi_i32(O[ft][2], p.pv_bm)),
+                         (uint32_t)clamp127(mulhi_i32(O[ft][3], p.pv_bm))),
+          ores, dst + ft * 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          pack4_lowbytes((uint32_t)requant_i8(O[ft][0], p.pv_b, p.pv_c),
+                         (uint32_t)requant_i8(O[ft][1], p.pv_b, p.pv_c),
+                         (uint32_t)requant_i8(O[ft][2], p.pv_b, p.pv_c),
+                         (uint32_t)requant_i8(O[ft][3], p.pv_b, p.pv_c)),
+          ores, dst + ft * 16, 0, 0);
+  }
+}
+
+// Polls of a work-queue word (each followed by s_sleep 1, about 64 clocks)
+// before a wave gives up; only a broken invariant could ever reach it.
+constexpr int kSpinLimit = 1 << 22;
+
 template <int D, int KT, bool BIAS, int VAR>
-__global__ __launch_bounds__(kThreads) void iqattn_fast(DevParams p) {
+__global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT, BIAS)) void iqattn_fast(
+    DevParams p) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  constexpr bool KSWZ = (D == 64);      // swizzled 64-byte K rows
-  constexpr int KSTR = KSWZ ? 64 : D + 16;
-  constexpr int KPL = D / 4;            // k-bytes per lane in the Q.K^T MFMA
-  constexpr int KS = (KT + 3) / 4;      // 64-key steps of the P.V MFMA
-  constexpr int NP = KT * 16;
+  constexpr int CW = fast_cw(KT, BIAS);         // compute waves; wave CW loads
+  constexpr int NBUF = fast_nbuf(KT, BIAS);
+  constexpr int R = fast_region_bytes(D, KT);  // bytes of one V, K or Q region
+  constexpr int BS = fast_nreg(KT, BIAS) * R;  // bytes of one buffer
+  constexpr bool QLDS = fast_nreg(KT, BIAS) == 3;
+  constexpr int KPL = D / 4;                   // k-bytes per lane in the Q.K^T MFMA
+  constexpr int KS = (KT + 3) / 4;             // 64-key steps of the P.V MFMA
   constexpr int FT = D / 16;
-  constexpr int K_BYTES = NP * KSTR;
-  constexpr bool VROW = (VAR == kFastLisValu);  // V row-major instead of V^T
-  constexpr int V_BYTES = VROW ? NP * D : KS * D * 64;
   typedef typename Mfma<D>::Op Op;
 
   const int N = p.n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
+  const int G = (int)gridDim.x;
 
-  // Work unit.  Blocks below n_full take one whole head; the heads left over
-  // for a last, partial round of blocks are split into quarter heads (query
-  // tiles q, q+4, ... for quarter q), so that round is a quarter as long.  The
-  // four quarters of a head sit 8 blocks apart: blocks are dealt to the 8
-  // XCDs round-robin, so they share an L2 for the K/V reads.
-  int u, qt0, qstep;
-  if ((int)blockIdx.x < p.n_full) {
-    u = blockIdx.x;
-    qt0 = (wave + kWaves - (u & (kWaves - 1))) & (kWaves - 1);  // rotate the extra tile
-    qstep = kWaves;
-  } else {
-    const int r = blockIdx.x - p.n_full;
-    const int k = r >> 3, q = k & 3;
-    u = p.n_full + (k >> 2) * 8 + (r & 7);
-    if (u >= p.units) return;  // uniform over the block, before any barrier
-    qt0 = q + 4 * wave;
-    qstep = 4 * kWaves;
-  }
+  const uint32_t smem0 = lds_addr(smem);
+  const char* sE = (const char*)(smem + NBUF * BS);
+  int32_t* sW = (int32_t*)(smem + NBUF * BS + kFastTableBytes);
+  // work-queue words: next tile of the workgroup's sequence, then per buffer
+  // the item it holds and the number of that item's tiles finished
+  int* ctl = (int*)(smem + NBUF * BS + kFastTableBytes + (VAR == kFastLisValu ? CW * 1024 : 0));
+  int* const ctl_next = ctl;
+  int* const ctl_ready = ctl + 1;
+  int* const ctl_done = ctl + 1 + NBUF;
 
-  int8_t* sK = smem;
-  int8_t* sV = smem + K_BYTES;
-  const char* sE = (const char*)(smem + K_BYTES + V_BYTES);
-  int32_t* sW = (int32_t*)(smem + K_BYTES + V_BYTES + (((p.exp_last + 1) * 4 + 15) & ~15));
-
-  const int64_t hbase = (int64_t)u * N * D;
-  const int8_t* gK = p.k + hbase;
-  const int8_t* gV = p.v + hbase;
-
-  // ---- stage K (rows >= N are zero)
-  for (int i = tid; i < NP * (D / 16); i += kThreads) {
-    const int row = i / (D / 16), c16 = i % (D / 16);
-    v4i val = {0, 0, 0, 0};
-    if (row < N) val = *(const v4i*)(gK + row * D + c16 * 16);
-    *(v4i*)(sK + (KSWZ ? swz64(row, c16) : row * KSTR + c16 * 16)) = val;
-  }
-  if (VROW) {
-    // ---- stage V row-major (rows >= N are zero)
-    for (int i = tid; i < NP * (D / 16); i += kThreads) {
-      const int row = i / (D / 16), c16 = i % (D / 16);
-      v4i val = {0, 0, 0, 0};
-      if (row < N) val = *(const v4i*)(gV + row * D + c16 * 16);
-      *(v4i*)(sV + row * D + c16 * 16) = val;
+  if (decode_item<KT>(p, blockIdx.x).u < 0) return;  // uniform, before the barrier
+  if (tid == 0) {
+    ctl_next[0] = 0;
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      ctl_ready[b] = -1;
+      ctl_done[b] = 0;
     }
-  } else {
-    // ---- stage V^T with the key permutation: a unit is 4 keys x 16 features
-    //      (four 16-byte loads), transposed in registers 4 x 4 bytes at a time;
-    //      keys 4q..4q+3 land on 4 contiguous bytes of each feature row
-    for (int i = tid; i < KS * 16 * FT; i += kThreads) {
-      const int kq = i % (KS * 16), fb = i / (KS * 16);
-      const int key0 = kq * 4;
-      const int8_t* src = gV + key0 * D + fb * 16;
-      v4i r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r[j] = v4i{0, 0, 0, 0};
-        if (key0 + j < N) r[j] = *(const v4i*)(src + j * D);
-      }
-      const int pos = vperm_pos(key0) & 63, c = pos >> 4;
-      int8_t* base = sV + (key0 >> 6) * (D * 64) + fb * 16 * 64 + (pos & 15);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = r[0][q], w1 = r[1][q], w2 = r[2][q], w3 = r[3][q];
-        const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-        const uint32_t b = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-        const uint32_t cc = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
-        const uint32_t d = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-        const uint32_t out[4] = {__builtin_amdgcn_perm(b, a, 0x05040100u),
-                                 __builtin_amdgcn_perm(b, a, 0x07060302u),
-                                 __builtin_amdgcn_perm(d, cc, 0x05040100u),
-                                 __builtin_amdgcn_perm(d, cc, 0x07060302u)};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int t = 4 * q + jj;  // feature within the block; row swizzle (t >> 1) & 3
-          *(uint32_t*)(base + t * 64 + 16 * (c ^ ((t >> 1) & 3))) = out[jj];
+  }
+  __syncthreads();  // the only workgroup barrier
+
+  if (wave == CW) {
+    // ---- loader wave: the exponential table (entries e << e_shift, 1 KB),
+    //      then item j of the workgroup's sequence into buffer j % NBUF once
+    //      every tile of item j - NBUF is finished; the table is in LDS
+    //      together with item 0
+    raw_buffer_load_lds(make_rsrc(p.exp_tab, kFastTableBytes), (lds_u32w*)(uintptr_t)lds_addr(sE),
+                        16, 16 * lane, 0, 0, 0);
+    for (int j = 0;; ++j) {
+      const Item it = decode_item<KT>(p, (int)blockIdx.x + j * G);
+      if (it.u < 0) break;
+      const int b = j % NBUF;
+      if (j >= NBUF) {
+        const int tprev = decode_item<KT>(p, (int)blockIdx.x + (j - NBUF) * G).T;
+        int spins = 0;
+        while (__hip_atomic_load(&ctl_done[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+               tprev) {
+          if (++spins > kSpinLimit) return;
+          __builtin_amdgcn_s_sleep(1);
         }
       }
+      if (lane == 0) __hip_atomic_store(&ctl_done[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      stage_head<D, R, QLDS>(p, it.u, smem0 + b * BS, lane);
+      __builtin_amdgcn_s_waitcnt(0);  // the item is in LDS
+      if (lane == 0) __hip_atomic_store(&ctl_ready[b], j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    return;
   }
-  // ---- stage the exponential table (entries e << e_shift)
-  {
-    uint32_t* dstE = (uint32_t*)sE;
-    for (int i = tid; i <= p.exp_last; i += kThreads) dstE[i] = p.exp_tab[i];
-  }
-  __syncthreads();
 
+  // ---- compute waves
   // padded keys of the last tile held by this lane: accumulator init and count
   v4i cmask;
   int npad = 0;
@@ -177,218 +260,266 @@ __global__ __launch_bounds__(kThreads) void iqattn_fast(DevParams p) {
     npad += pad ? 1 : 0;
   }
   const int32_t tab0 = (int32_t)lds_addr(sE);  // absolute LDS address of entry 0
-  // per-lane operand offsets (swizzled rows: the swizzle depends on li only)
-  const int koff = KSWZ ? swz64(li, g) : li * KSTR + KPL * g;
-  const int voff = swz64(li, g);
-  const int h = u % p.heads;
+  // per-lane operand offsets inside a K region (the swizzle depends on li only)
+  const int koff = (D == 64 ? li * 64 + 16 * g : li * 32 + 8 * g) ^ (kswz<D>(li) << 4);
+  // transpose-read offsets inside a 64-key block of a V region: lane (g, 2b + h)
+  // reads 8 features (16 ft + 8 h ...) of key 16 (2 hr + (b >> 2)) + 4 g + (b & 3)
+  // for read hr; the chunk index (ft) enters by XOR
+  int vtr[2];
+#pragma unroll
+  for (int hr = 0; hr < 2; ++hr) {
+    const int kap = 16 * (2 * hr + (li >> 3)) + 4 * g + ((li >> 1) & 3);
+    vtr[hr] = kap * D + 8 * (li & 1) + 16 * vswz<D>(kap);
+  }
   const int32_t qk_bm = p.qk_bm;
   const int32_t lpad = mulhi_i32(p.mask_s, qk_bm);
 
-  for (int qt = qt0; qt < KT; qt += qstep) {
-    const int qrow = qt * 16 + li;
-    Op qop = Op{};
-    if (qrow < N) qop = *(const Op*)(p.q + hbase + (int64_t)qrow * D + KPL * g);
-
-    // ---- S^T = K . Q^T (+ bias / padding mask in the accumulator).  K
-    //      operands are read one tile ahead; the scheduling barriers keep the
-    //      compiler from hoisting every LDS read of a phase (registers)
-    v4i S[KT];
-    Op knext = *(const Op*)(sK + koff);
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const Op kop = knext;
-      if (kt + 1 < KT) knext = *(const Op*)(sK + (kt + 1) * 16 * KSTR + koff);
-      v4i c0 = {0, 0, 0, 0};
-      if (BIAS) {
-        c0 = *(const v4i*)(p.bias + ((int64_t)h * NP + qrow) * NP + kt * 16 + 4 * g);
-      } else if (kt == KT - 1) {
-        c0 = cmask;
+  int jw = 0, base = 0, have = -1;
+  Item it = decode_item<KT>(p, blockIdx.x);
+  // tile numbers are taken one tile ahead, so the atomic's latency is hidden
+  int sq = 0;
+  if (lane == 0) sq = __hip_atomic_fetch_add(ctl_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (;;) {
+    // this tile of the workgroup's sequence: item jw, tile s - base of it
+    const int s = __builtin_amdgcn_readfirstlane(sq);
+    if (lane == 0) sq = __hip_atomic_fetch_add(ctl_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (it.u >= 0 && s >= base + it.T) {
+      base += it.T;
+      ++jw;
+      it = decode_item<KT>(p, (int)blockIdx.x + jw * G);
+    }
+    if (it.u < 0) break;
+    const int b = jw % NBUF;
+    if (have < jw) {
+      int spins = 0;
+      while (__hip_atomic_load(&ctl_ready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != jw) {
+        if (++spins > kSpinLimit) return;
+        __builtin_amdgcn_s_sleep(1);
       }
-      S[kt] = Mfma<D>::run(kop, qop, c0);
-      __builtin_amdgcn_sched_barrier(0);
+      have = jw;
     }
+    const int qt = it.qt0 + (s - base) * it.qstep;
 
-    // ---- pass 1: row max of the accumulators (plain code: these are the first
-    //      reads of the MFMA results)
-    int32_t amax = max(S[0][0], S[0][1]);
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt > 0) amax = max(amax, max(S[kt][0], S[kt][1]));
-      amax = max(amax, max(S[kt][2], S[kt][3]));
-    }
-    amax = wave_max4(amax);
-    const int32_t m = clamp127(mulhi_i32(amax, qk_bm));
-    // table address of index (m - L) is rb - 4 L; saturating L to [-127, 127]
-    // clamps it to [lo, hi] (entries past exp_last are 0)
-    const int32_t rb = tab0 + m * 4;
-    const int32_t lo = rb - 127 * 4;
-    const int32_t hi = tab0 + min(m + 127, p.exp_last) * 4;
+    const uint32_t vbase = smem0 + b * BS;  // V region; K (and Q) regions follow
+    const int8_t* sV = smem + b * BS;
+    const int8_t* sK = sV + R;
+    const int8_t* sQ = sV + 2 * R;
+    const int u = it.u;
+    const int64_t hbase = (int64_t)u * N * D;
+    const int h = u % p.heads;
+    // Query rows past N are clamped to N - 1 for every load, bias read and
+    // store: such a lane computes query N - 1 exactly and stores the same bytes.
+    const __amdgpu_buffer_rsrc_t qres = buf_rsrc(p.q + hbase, (uint32_t)(N * D));
+    const __amdgpu_buffer_rsrc_t ores = buf_rsrc(p.out + hbase, (uint32_t)(N * D));
 
-    // ---- pass 2: e << e_shift from the table, row sum
-    uint32_t s = 0;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t a = exp_offset(S[kt][r], qk_bm, -4, rb, lo, hi);
-        const uint32_t e = lds_read_u32((uint32_t)a);
-        S[kt][r] = (int32_t)e;
-        s += e;
-      }
-    }
-    if (npad) s -= (uint32_t)npad * lds_read_u32((uint32_t)min(max(rb - lpad * 4, lo), hi));
-    s = wave_sum4(s);
-    const uint32_t st = s >> p.e_shift;
+    {
+      const int qrow = min(qt * 16 + li, N - 1);
+      Op qop;
+      if (QLDS)
+        qop = *(const Op*)(sQ + ((D == 64 ? qrow * 64 + 16 * g : qrow * 32 + 8 * g) ^
+                                 (kswz<D>(qrow) << 4)));
+      else
+        qop = buf_load<Op>(qres, qrow * D + KPL * g);
 
-    // ---- IntDiv: f = floor(2^M / st).  |estimate - 2^M/st| <= 1/2 (2^M/st
-    //      <= 2^22, one-ulp reciprocal), so the truncated estimate is off by at
-    //      most one; f st < 2^31 keeps 32 bits exact
-    const uint32_t two_m = 1u << p.intdiv_m;
-    uint32_t f = (uint32_t)(__builtin_amdgcn_rcpf((float)st) * (float)two_m);
-    int32_t rem = (int32_t)(two_m - f * st);
-    if (rem < 0) { f -= 1; rem += (int32_t)st; }
-    if (rem >= (int32_t)st) { f += 1; }
-    // Shiftmax: one key holding the whole row would give P = 2^(k_out-1); f - 1
-    // yields the clamped 2^(k_out-1) - 1 for it (every other key has e = 0)
-    if (VAR == kFastShiftmax && p.e0_pow2 && st == (uint32_t)p.e0) f -= 1;
-    const uint32_t F = f << p.f_shift;
-    __builtin_amdgcn_sched_barrier(0);
-
-    if (VAR == kFastShiftmax) {
-      // ---- P = (f e) >> (M - k_out + 1) as one mulhi, O^T = V^T . P^T
-      v4i O[FT];
+      // ---- S^T = K . Q^T (+ bias / padding mask in the accumulator).  K
+      //      operands are read one tile ahead; the scheduling barriers keep the
+      //      compiler from hoisting every LDS read of a phase (registers)
+      constexpr int KPF = 3;  // K operand reads in flight ahead of the MFMA
+      v4i S[KT];
+      Op kb[KPF];
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) O[ft] = v4i{0, 0, 0, 0};
+      for (int i = 0; i < KPF; ++i)
+        if (i < KT) kb[i] = *(const Op*)(sK + i * 16 * D + koff);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        v4i pop;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int kt = ks * 4 + tt;
-          uint32_t word = 0;
-          if (kt < KT)
-            word = p4_pack((uint32_t)S[kt][0], (uint32_t)S[kt][1], (uint32_t)S[kt][2],
-                           (uint32_t)S[kt][3], F);
-          pop[tt] = (int32_t)word;
+      for (int kt = 0; kt < KT; ++kt) {
+        const Op kop = kb[kt % KPF];
+        if (kt + KPF < KT) kb[kt % KPF] = *(const Op*)(sK + (kt + KPF) * 16 * D + koff);
+        v4i c0 = {0, 0, 0, 0};
+        if (BIAS) {
+          c0 = *(const v4i*)(p.bias + ((int64_t)h * (KT * 16) + qrow) * (KT * 16) + kt * 16 + 4 * g);
+        } else if (kt == KT - 1) {
+          c0 = cmask;
         }
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          const v4i vop = *(const v4i*)(sV + ks * (D * 64) + ft * 16 * 64 + voff);
-          O[ft] = mfma64(vop, pop, O[ft]);
-        }
+        S[kt] = Mfma<D>::run(kop, qop, c0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // lane holds features 16 ft + 4 g + r of query qrow
-      if (qrow < N) {
-        int8_t* dst = p.out + hbase + (int64_t)qrow * D + 4 * g;
-        if (p.pv_fast) {
+
+      // ---- pass 1: row max of the accumulators (plain code: these are the first
+      //      reads of the MFMA results)
+      // (four independent chains)
+      int32_t mx[4] = {S[0][0], S[0][1], S[0][2], S[0][3]};
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft)
-            *(uint32_t*)(dst + ft * 16) = pack4_lowbytes(
-                (uint32_t)clamp127(mulhi_i32(O[ft][0], p.pv_bm)),
-                (uint32_t)clamp127(mulhi_i32(O[ft][1], p.pv_bm)),
-                (uint32_t)clamp127(mulhi_i32(O[ft][2], p.pv_bm)),
-                (uint32_t)clamp127(mulhi_i32(O[ft][3], p.pv_bm)));
-        } else {
+      for (int kt = 1; kt + 1 < KT; kt += 2)
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft)
-            *(uint32_t*)(dst + ft * 16) = pack4_lowbytes(
-                (uint32_t)requant_i8(O[ft][0], p.pv_b, p.pv_c),
-                (uint32_t)requant_i8(O[ft][1], p.pv_b, p.pv_c),
-                (uint32_t)requant_i8(O[ft][2], p.pv_b, p.pv_c),
-                (uint32_t)requant_i8(O[ft][3], p.pv_b, p.pv_c));
+        for (int r = 0; r < 4; ++r) mx[r] = max(mx[r], max(S[kt][r], S[kt + 1][r]));  // v_max3
+      if ((KT & 1) == 0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = max(mx[r], S[KT - 1][r]);
+      int32_t amax = max(max(mx[0], mx[1]), max(mx[2], mx[3]));
+      amax = wave_max4(amax);
+      const int32_t m = clamp127(mulhi_i32(amax, qk_bm));
+      // table address of index (m - L) is rb - 4 L; saturating L to [-127, 127]
+      // clamps it to [lo, hi] (entries past exp_last are 0)
+      const int32_t rb = tab0 + m * 4;
+      const int32_t lo = rb - 127 * 4;
+      const int32_t hi = tab0 + min(m + 127, p.exp_last) * 4;
+
+      // ---- pass 2: e << e_shift from the table, row sum (two chains)
+      uint32_t sacc[2] = {0, 0};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t a = exp_offset(S[kt][r], qk_bm, -4, rb, lo, hi);
+          const uint32_t e = lds_read_u32((uint32_t)a);
+          S[kt][r] = (int32_t)e;
+          sacc[r >> 1] += e;
         }
       }
-    } else {
-      // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code
-      const int32_t Fl = p.lis_f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[kt][r] = lis_shift(mulhi_u32((uint32_t)S[kt][r], F), Fl);
+      uint32_t s = sacc[0] + sacc[1];
+      if (npad) s -= (uint32_t)npad * lds_read_u32((uint32_t)min(max(rb - lpad * 4, lo), hi));
+      s = wave_sum4(s);
+      const uint32_t st = s >> p.e_shift;
 
-      if (VAR == kFastLisMfma) {
-        // ---- o = -(O_0 + 256 O_1), O_h = V^T . (plane h of -2^w)^T
-        v4i O0[FT], O1[FT];
+      // ---- IntDiv: f = floor(2^M / st).  |estimate - 2^M/st| <= 1/2 (2^M/st
+      //      <= 2^22, one-ulp reciprocal), so the truncated estimate is off by at
+      //      most one; f st < 2^31 keeps 32 bits exact
+      const uint32_t two_m = 1u << p.intdiv_m;
+      uint32_t f = (uint32_t)(__builtin_amdgcn_rcpf((float)st) * (float)two_m);
+      int32_t rem = (int32_t)(two_m - f * st);
+      if (rem < 0) { f -= 1; rem += (int32_t)st; }
+      if (rem >= (int32_t)st) { f += 1; }
+      // Shiftmax: one key holding the whole row would give P = 2^(k_out-1); f - 1
+      // yields the clamped 2^(k_out-1) - 1 for it (every other key has e = 0)
+      if (VAR == kFastShiftmax && p.e0_pow2 && st == (uint32_t)p.e0) f -= 1;
+      const uint32_t F = f << p.f_shift;
+      __builtin_amdgcn_sched_barrier(0);
+
+      if (VAR == kFastShiftmax) {
+        // ---- P = (f e) >> (M - k_out + 1) as one mulhi, O^T = V^T . P^T; the
+        //      V^T operands of the next 64-key step are read during this one
+        v4i O[FT];
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) O0[ft] = O1[ft] = v4i{0, 0, 0, 0};
+        for (int ft = 0; ft < FT; ++ft) O[ft] = v4i{0, 0, 0, 0};
+        v4i vcur[FT], vnxt[FT];
+        read_vt<D, FT>(vbase, vtr, vcur);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          v4i plo, phi;
+          if (ks + 1 < KS) read_vt<D, FT>(vbase + (ks + 1) * 64 * D, vtr, vnxt);
+          v4i pop;
+          if (ks * 4 + 3 < KT && p.p_u24) {
+            p16_pack24(S[ks * 4], S[ks * 4 + 1], S[ks * 4 + 2], S[ks * 4 + 3], F, pop);
+          } else {
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const int kt = ks * 4 + tt;
-            int32_t lo_w = 0, hi_w = 0;
-            if (kt < KT) lis_planes(S[kt], lo_w, hi_w);
-            plo[tt] = lo_w;
-            phi[tt] = hi_w;
-          }
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft) {
-            const v4i vop = *(const v4i*)(sV + ks * (D * 64) + ft * 16 * 64 + voff);
-            O0[ft] = mfma64(vop, plo, O0[ft]);
-            O1[ft] = mfma64(vop, phi, O1[ft]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (qrow < N) {
-          int8_t* dst = p.out + hbase + (int64_t)qrow * D + 4 * g;
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft) {
-            int32_t y[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int32_t o = -(O0[ft][r] + (O1[ft][r] << 8));
-              y[r] = p.pv_fast ? clamp127(mulhi_i32(o, p.pv_bm)) : requant_i8(o, p.pv_b, p.pv_c);
+            for (int tt = 0; tt < 4; ++tt) {
+              const int kt = ks * 4 + tt;
+              uint32_t word = 0;
+              if (kt < KT)
+                word = p4_pack((uint32_t)S[kt][0], (uint32_t)S[kt][1], (uint32_t)S[kt][2],
+                               (uint32_t)S[kt][3], F);
+              pop[tt] = (int32_t)word;
             }
-            *(uint32_t*)(dst + ft * 16) =
-                pack4_lowbytes((uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]);
           }
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) O[ft] = mfma64(vcur[ft], pop, O[ft]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
         }
+        // lane holds features 16 ft + 4 g + r of query qrow
+        store_out<FT>(p, O, ores, qrow * D + 4 * g);
       } else {
-        // ---- VALU P.V: lane owns feature t of QPL queries; the wave's shifts
-        //      go through LDS one 16-key tile at a time (16 keys x 16 queries)
-        constexpr int QPL = 16 * D / 64;
-        const int t = lane % D;
-        const int qsub = (lane / D) * QPL;
-        int32_t* sWw = sW + wave * 256;
-        int32_t o[QPL];
+        // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code
+        const int32_t Fl = p.lis_f;
 #pragma unroll
-        for (int i = 0; i < QPL; ++i) o[i] = 0;
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+          for (int r = 0; r < 4; ++r) S[kt][r] = lis_shift(mulhi_u32((uint32_t)S[kt][r], F), Fl);
+
+        if (VAR == kFastLisMfma) {
+          // ---- o = -(O_0 + 256 O_1), O_h = V^T . (plane h of -2^w)^T
+          v4i O0[FT], O1[FT];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sWw[(4 * g + r) * 16 + li] = S[kt][r];
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 4
-          for (int jj = 0; jj < 16; ++jj) {
-            const int32_t vj = (int32_t)sV[(kt * 16 + jj) * D + t];  // 0 for padded keys
-            const v4i* wrow = (const v4i*)(sWw + jj * 16 + qsub);
+          for (int ft = 0; ft < FT; ++ft) O0[ft] = O1[ft] = v4i{0, 0, 0, 0};
+          v4i vcur[FT], vnxt[FT];
+          read_vt<D, FT>(vbase, vtr, vcur);
 #pragma unroll
-            for (int i4 = 0; i4 < QPL / 4; ++i4) {
-              const v4i w4 = wrow[i4];
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) read_vt<D, FT>(vbase + (ks + 1) * 64 * D, vtr, vnxt);
+            v4i plo, phi;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) o[4 * i4 + r] += (int32_t)((uint32_t)vj << w4[r]);
+            for (int tt = 0; tt < 4; ++tt) {
+              const int kt = ks * 4 + tt;
+              int32_t lo_w = 0, hi_w = 0;
+              if (kt < KT) lis_planes(S[kt], lo_w, hi_w);
+              plo[tt] = lo_w;
+              phi[tt] = hi_w;
             }
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
-        for (int i = 0; i < QPL; ++i) {
-          const int qi = qt * 16 + qsub + i;
-          if (qi < N) {
-            const int32_t y = p.pv_fast ? clamp127(mulhi_i32(o[i], p.pv_bm))
-                                        : requant_i8(o[i], p.pv_b, p.pv_c);
-            p.out[hbase + (int64_t)qi * D + t] = (int8_t)y;
+            for (int ft = 0; ft < FT; ++ft) {
+              O0[ft] = mfma64(vcur[ft], plo, O0[ft]);
+              O1[ft] = mfma64(vcur[ft], phi, O1[ft]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
+          }
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O0[ft][r] = -(O0[ft][r] + (O1[ft][r] << 8));
+          store_out<FT>(p, O0, ores, qrow * D + 4 * g);
+        } else {
+          // ---- VALU P.V: lane owns feature t of QPL queries; the wave's shifts
+          //      go through LDS one 16-key tile at a time (16 keys x 16 queries)
+          constexpr int QPL = 16 * D / 64;
+          const int t = lane % D;
+          const int qsub = (lane / D) * QPL;
+          int32_t* sWw = sW + wave * 256;
+          int32_t o[QPL];
+#pragma unroll
+          for (int i = 0; i < QPL; ++i) o[i] = 0;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sWw[(4 * g + r) * 16 + li] = S[kt][r];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 4
+            for (int jj = 0; jj < 16; ++jj) {
+              const int row = kt * 16 + jj;  // rows >= N are zero
+              const int32_t vj = (int32_t)sV[row * D + (t ^ (vswz<D>(row) << 4))];
+              const v4i* wrow = (const v4i*)(sWw + jj * 16 + qsub);
+#pragma unroll
+              for (int i4 = 0; i4 < QPL / 4; ++i4) {
+                const v4i w4 = wrow[i4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[4 * i4 + r] += (int32_t)((uint32_t)vj << w4[r]);
+              }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (p.pv_fast) {
+#pragma unroll
+            for (int i = 0; i < QPL; ++i)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)clamp127(mulhi_i32(o[i], p.pv_bm)), ores,
+                                                   min(qt * 16 + qsub + i, N - 1) * D + t, 0, 0);
+          } else {
+#pragma unroll
+            for (int i = 0; i < QPL; ++i)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)requant_i8(o[i], p.pv_b, p.pv_c), ores,
+                                                   min(qt * 16 + qsub + i, N - 1) * D + t, 0, 0);
           }
         }
       }
     }
+    // this tile's LDS reads have returned: count it against the buffer
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (lane == 0) __hip_atomic_fetch_add(&ctl_done[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
