@@ -235,7 +235,7 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
       const int var = fast_variant(p);
       const bool bias = p->rel_bias != NULL;
       const size_t R = (size_t)fast_region_bytes(D, KT);
-      const size_t nbuf = (size_t)fast_nbuf(KT, bias);
+      const size_t nbuf = (size_t)fast_nbuf(KT, bias, var);
       const size_t cw = (size_t)fast_cw(KT, bias);
       const size_t bs = (size_t)fast_nreg(KT, bias) * R;  // bytes per buffer
       const size_t used = nbuf * bs + kFastTableBytes + (var == kFastLisValu ? cw * 1024 : 0) + 64;

@@ -226,14 +226,17 @@ __device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t b0, uint32_t b1, uin
 // let the next head's loads run under the current head's compute; the
 // exponential table and the LIS shift scratch follow.
 constexpr int fast_region_bytes(int d, int kt) { return ((kt * 16 * d + 1023) / 1024) * 1024; }
-// Rows of up to 256 keys without a bias table run one workgroup per CU: 15
-// compute waves and one loader wave over three (V, K, Q) buffers, so that the
-// waves of a CU share one tile queue (two workgroups on a CU drift apart: the
-// older one's waves win the issue arbitration and the younger one finishes
-// alone).  Longer rows (about 250 VGPRs per lane) and bias-table rows use
-// 3 compute waves, one (V, K) buffer, and several workgroups per CU.
-constexpr bool fast_big(int kt, bool bias) { return !bias && kt <= 16; }
-constexpr int fast_nbuf(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 1; }
+// Rows of up to 256 keys run workgroups of 15 compute waves and one loader
+// wave over four (V, K, Q) buffers (three for the LIS VALU back end, whose
+// shift scratch needs the room); at 197 keys one such workgroup fills a CU,
+// so all waves of a CU share one tile queue (two workgroups on a CU drift
+// apart: the older one's waves win the issue arbitration and the younger one
+// finishes alone).  Longer rows (about 250 VGPRs per lane) use 3 compute waves
+// and one (V, K) buffer, two workgroups per CU.
+constexpr bool fast_big(int kt, bool bias) { return kt <= 16; }
+constexpr int fast_nbuf(int kt, bool bias, int var) {
+  return fast_big(kt, bias) ? (var == kFastLisValu ? 3 : 4) : 1;
+}
 constexpr int fast_nreg(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 2; }
 constexpr int fast_cw(int kt, bool bias) { return fast_big(kt, bias) ? 15 : 3; }
 // minimum waves per SIMD the register allocation must allow

@@ -112,8 +112,8 @@ __device__ __forceinline__ Item decode_item(const DevParams& p, int k) {
   return it;
 }
 
-// Direct loads of head u's V, K (and Q) (R / 1024 blocks each) into the LDS
-// regions at vbuf, vbuf + R (and vbuf + 2R), issued by one wave.  Lane l of block i fills LDS bytes
+// Direct loads of head u's K (and Q), then V (R / 1024 blocks each) into the
+// LDS regions at vbuf + R (and vbuf + 2R) and vbuf, issued by one wave.  Lane l of block i fills LDS bytes
 // [1024 i + 16 l, +16) = (row, chunk position cp) from source chunk
 // cp ^ swizzle(row).  Rows >= N lie past the buffer range and arrive as zeros.
 template <int D, int R, bool WITH_Q>
@@ -129,13 +129,22 @@ __device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t v
     const int o = blk * 1024 + 16 * lane;
     const int row = o / D, cp = (o % D) >> 4;
     const int ko = row * D + 16 * (cp ^ kswz<D>(row));
-    raw_buffer_load_lds(rv, (lds_u32w*)(uintptr_t)(vbuf + blk * 1024), 16,
-                        row * D + 16 * (cp ^ vswz<D>(row)), 0, 0, 0);
     raw_buffer_load_lds(rk, (lds_u32w*)(uintptr_t)(vbuf + R + blk * 1024), 16, ko, 0, 0, 0);
     if (WITH_Q)
       raw_buffer_load_lds(rq, (lds_u32w*)(uintptr_t)(vbuf + 2 * R + blk * 1024), 16, ko, 0, 0, 0);
   }
+  // V last: the Q.K^T part of a tile may start once the loads above are in
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int o = blk * 1024 + 16 * lane;
+    const int row = o / D, cp = (o % D) >> 4;
+    raw_buffer_load_lds(rv, (lds_u32w*)(uintptr_t)(vbuf + blk * 1024), 16,
+                        row * D + 16 * (cp ^ vswz<D>(row)), 0, 0, 0);
+  }
 }
+
+// s_waitcnt immediate for vmcnt(n), other counters untouched (n < 64)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // V^T operands of one 64-key step (FT 16-feature tiles) by transpose reads:
 // two ds_read_b64_tr_b8 per tile at the lane offsets vtr[0], vtr[1], the
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
     DevParams p) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   constexpr int CW = fast_cw(KT, BIAS);         // compute waves; wave CW loads
-  constexpr int NBUF = fast_nbuf(KT, BIAS);
+  constexpr int NBUF = fast_nbuf(KT, BIAS, VAR);
   constexpr int R = fast_region_bytes(D, KT);  // bytes of one V, K or Q region
   constexpr int BS = fast_nreg(KT, BIAS) * R;  // bytes of one buffer
   constexpr bool QLDS = fast_nreg(KT, BIAS) == 3;
@@ -209,6 +218,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   int* const ctl_next = ctl;
   int* const ctl_ready = ctl + 1;
   int* const ctl_done = ctl + 1 + NBUF;
+  int* const ctl_vready = ctl + 1 + 2 * NBUF;  // item whose V is in the buffer
 
   if (decode_item<KT>(p, blockIdx.x).u < 0) return;  // uniform, before the barrier
   if (tid == 0) {
@@ -217,6 +227,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
     for (int b = 0; b < NBUF; ++b) {
       ctl_ready[b] = -1;
       ctl_done[b] = 0;
+      ctl_vready[b] = -1;
     }
   }
   __syncthreads();  // the only workgroup barrier
@@ -243,8 +254,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       }
       if (lane == 0) __hip_atomic_store(&ctl_done[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       stage_head<D, R, QLDS>(p, it.u, smem0 + b * BS, lane);
-      __builtin_amdgcn_s_waitcnt(0);  // the item is in LDS
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(R / 1024));  // K and Q are in LDS
       if (lane == 0) __hip_atomic_store(&ctl_ready[b], j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __builtin_amdgcn_s_waitcnt(0);  // and V
+      if (lane == 0) __hip_atomic_store(&ctl_vready[b], j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     return;
   }
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   const int32_t qk_bm = p.qk_bm;
   const int32_t lpad = mulhi_i32(p.mask_s, qk_bm);
 
-  int jw = 0, base = 0, have = -1;
+  int jw = 0, base = 0, have = -1, havev = -1;
   Item it = decode_item<KT>(p, blockIdx.x);
   // tile numbers are taken one tile ahead, so the atomic's latency is hidden
   int sq = 0;
@@ -289,6 +302,8 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       it = decode_item<KT>(p, (int)blockIdx.x + jw * G);
     }
     if (it.u < 0) break;
+    // the workgroup's last item runs at the highest priority (its tiles end the kernel)
+    const bool last_item = decode_item<KT>(p, (int)blockIdx.x + (jw + 1) * G).u < 0;
     const int b = jw % NBUF;
     if (have < jw) {
       int spins = 0;
@@ -344,6 +359,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
         __builtin_amdgcn_sched_barrier(0);
       }
 
+      if (last_item)
+        __builtin_amdgcn_s_setprio(3);
+      else
+        __builtin_amdgcn_s_setprio(2);
       // ---- pass 1: row max of the accumulators (plain code: these are the first
       //      reads of the MFMA results)
       // (four independent chains)
@@ -393,6 +412,15 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       // yields the clamped 2^(k_out-1) - 1 for it (every other key has e = 0)
       if (VAR == kFastShiftmax && p.e0_pow2 && st == (uint32_t)p.e0) f -= 1;
       const uint32_t F = f << p.f_shift;
+      // V of the item (loaded after K and Q) is needed from here on
+      if (havev < jw) {
+        int spins = 0;
+        while (__hip_atomic_load(&ctl_vready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != jw) {
+          if (++spins > kSpinLimit) return;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        havev = jw;
+      }
       __builtin_amdgcn_sched_barrier(0);
 
       if (VAR == kFastShiftmax) {
@@ -517,6 +545,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // this tile's LDS reads have returned: count it against the buffer
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     if (lane == 0) __hip_atomic_fetch_add(&ctl_done[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
