@@ -9,6 +9,16 @@
 
 using namespace iqattn;
 
+namespace iqattn {
+// last HIP error text of this thread, for iqattn_strerror(IQATTN_E_LAUNCH)
+thread_local char g_errbuf[256];
+
+int set_hip_error(hipError_t e, const char* what) {
+  snprintf(g_errbuf, sizeof(g_errbuf), "%s: %s", what, hipGetErrorString(e));
+  return IQATTN_E_LAUNCH;
+}
+}  // namespace iqattn
+
 namespace {
 
 // e(-idx) << shift for idx = 0..255: the Shiftmax exponential of
@@ -41,13 +51,6 @@ __global__ void iqattn_expand_bias(int32_t* out, const int32_t* table, int32_t h
     }
     out[x] = val;
   }
-}
-
-thread_local char g_errbuf[256];
-
-int set_hip_error(hipError_t e, const char* what) {
-  snprintf(g_errbuf, sizeof(g_errbuf), "%s: %s", what, hipGetErrorString(e));
-  return IQATTN_E_LAUNCH;
 }
 
 int validate(const iqattn_params* p) {

@@ -285,6 +285,9 @@ __device__ __forceinline__ v4i mfma64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// records the HIP error text for iqattn_strerror and returns IQATTN_E_LAUNCH
+int set_hip_error(hipError_t e, const char* what);
+
 // host-side selectors, one per translation unit
 KernelFn generic_kernel(int d, int ktm, int variant, bool bias);
 KernelFn fast_kernel(int d, int kt, bool bias, int var);  // null if not instantiated

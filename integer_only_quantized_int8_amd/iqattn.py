@@ -30,8 +30,11 @@ IQATTN_LIS = 1
 IQATTN_LIS_VALU = 0
 IQATTN_LIS_MFMA = 1
 IQATTN_MAX_SEQ = 640
+IQLINEAR_PLAIN = 0
+IQLINEAR_QKV_HEADS = 1
 
-EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror")
+EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
+            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy")
 
 
 class iqattn_params(C.Structure):
@@ -39,6 +42,12 @@ class iqattn_params(C.Structure):
         "batch", "heads", "seq_len", "head_dim", "qk_b", "qk_c", "pv_b", "pv_c", "i0",
         "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "lis_engine", "window")] + \
         [("rel_bias", C.POINTER(C.c_int32))]
+
+
+class iqlinear_params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "rows", "in_features", "out_features", "layout", "batch", "seq_len", "heads",
+        "head_dim")] + [("b", C.c_int32 * 3), ("c", C.c_int32 * 3)]
 
 
 class IQAttnError(RuntimeError):
@@ -66,6 +75,12 @@ def load_library():
         lib.iqattn_destroy.restype = C.c_int
         lib.iqattn_strerror.argtypes = [C.c_int]
         lib.iqattn_strerror.restype = C.c_char_p
+        lib.iqlinear_create.argtypes = [C.POINTER(iqlinear_params), C.POINTER(C.c_void_p)]
+        lib.iqlinear_create.restype = C.c_int
+        lib.iqlinear_forward.argtypes = [C.c_void_p] * 7
+        lib.iqlinear_forward.restype = C.c_int
+        lib.iqlinear_destroy.argtypes = [C.c_void_p]
+        lib.iqlinear_destroy.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -149,6 +164,85 @@ class IQAttn:
     def close(self):
         if self.ctx:
             iqattn_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- linear layer
+def make_linear_params(params: Dict[str, object]) -> iqlinear_params:
+    """Fill an iqlinear_params from a dict (rows, in_features, out_features,
+    layout, batch, seq_len, heads, head_dim, b, c; b and c are 1- or 3-tuples)."""
+    p = iqlinear_params()
+    for name in ("rows", "in_features", "out_features", "layout", "batch", "seq_len", "heads",
+                 "head_dim"):
+        setattr(p, name, int(params.get(name, 0) or 0))
+    b = list(params["b"]) + [1] * 3
+    c = list(params["c"]) + [0] * 3
+    for i in range(3):
+        p.b[i] = int(b[i])
+        p.c[i] = int(c[i])
+    return p
+
+
+def iqlinear_create(p: iqlinear_params) -> int:
+    ctx = C.c_void_p()
+    rc = load_library().iqlinear_create(C.byref(p), C.byref(ctx))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinear_create")
+    return ctx.value
+
+
+def iqlinear_forward(ctx: int, x, w, out0, out1=None, out2=None, stream=None) -> None:
+    """Enqueue the int8 linear layer on `stream` (default: torch's current stream)."""
+    ptr = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    rc = load_library().iqlinear_forward(C.c_void_p(ctx), ptr(x), ptr(w), ptr(out0), ptr(out1),
+                                         ptr(out2), C.c_void_p(_stream_handle(stream)))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinear_forward")
+
+
+def iqlinear_destroy(ctx: Optional[int]) -> None:
+    rc = load_library().iqlinear_destroy(C.c_void_p(ctx) if ctx else None)
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinear_destroy")
+
+
+class IQLinear:
+    """Owns one linear-layer context: x [rows, in] int8, w [out, in] int8."""
+
+    def __init__(self, params: Dict[str, object]):
+        self.params = dict(params)
+        self.ctx = iqlinear_create(make_linear_params(self.params))
+
+    def forward(self, x, w, outs=None, stream=None):
+        import torch
+        P = self.params
+        rows, fin, fout = P["rows"], P["in_features"], P["out_features"]
+        for name, t, shape in (("x", x, (rows, fin)), ("w", w, (fout, fin))):
+            if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() \
+                    or tuple(t.shape) != shape:
+                raise ValueError(f"{name} must be a contiguous int8 device tensor of shape {shape}")
+        if P["layout"] == IQLINEAR_QKV_HEADS:
+            shape = (P["batch"], P["heads"], P["seq_len"], P["head_dim"])
+            if outs is None:
+                outs = tuple(torch.empty(shape, dtype=torch.int8, device=x.device) for _ in range(3))
+            iqlinear_forward(self.ctx, x, w, outs[0], outs[1], outs[2], stream)
+            return outs
+        out = outs if outs is not None else torch.empty((rows, fout), dtype=torch.int8,
+                                                        device=x.device)
+        iqlinear_forward(self.ctx, x, w, out, None, None, stream)
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if self.ctx:
+            iqlinear_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):

@@ -36,6 +36,7 @@ _CHUNK = 1 << 22
 
 # Stream ids (one independent SplitMix64 stream per use).
 S_Q, S_K, S_V, S_PARAMS, S_SIGMA, S_OUTLIER, S_BIAS = 1, 2, 3, 4, 5, 6, 7
+S_X, S_W, S_LPARAMS = 8, 9, 10
 
 SHIFTMAX = 0
 LIS = 1
@@ -184,3 +185,51 @@ def config_workload(cfg: int, seed: Optional[int] = None) -> Workload:
 def config_shape(cfg: int):
     s = CONFIGS[cfg]
     return s["batch"], s["heads"], s["seq_len"], s["head_dim"]
+
+
+# ---------------------------------------------------------------- linear layers
+@dataclass
+class LinearWorkload:
+    """int8 activations x [rows, in], weights w [out, in] and the layer's
+    parameters (a dict accepted by iqattn.IQLinear)."""
+    name: str
+    x: np.ndarray
+    w: np.ndarray
+    params: Dict[str, object] = field(default_factory=dict)
+
+
+def make_linear(rows: int, in_features: int, out_features: int, seed: int, sigma_x=24.0,
+                sigma_w=24.0, qkv_heads: Optional[tuple] = None, name: str = "linear",
+                target_sigma=32.0) -> LinearWorkload:
+    """Seeded int8 x and w (clipped Gaussians) and dyadic pairs: b uniform in
+    [2^14, 2^15), c chosen so that b / 2^c maps the accumulator's standard
+    deviation sqrt(in) * sigma_x * sigma_w to about target_sigma.
+    qkv_heads = (batch, seq_len, heads, head_dim) selects the head-split layout
+    (out = 3 * heads * head_dim, one pair per Q, K, V)."""
+    x = int8_gaussian(Stream(seed, S_X), (rows, in_features), sigma_x)
+    w = int8_gaussian(Stream(seed, S_W), (out_features, in_features), sigma_w)
+    st = Stream(seed, S_LPARAMS)
+    npairs = 3 if qkv_heads else 1
+    b = st.randint(1 << 14, (1 << 15) - 1, npairs)
+    sd = float(np.sqrt(in_features)) * sigma_x * sigma_w
+    c = [int(np.ceil(np.log2(float(bi) * sd / target_sigma))) for bi in b]
+    params = dict(rows=rows, in_features=in_features, out_features=out_features,
+                  layout=0, batch=0, seq_len=0, heads=0, head_dim=0,
+                  b=tuple(int(v) for v in b), c=tuple(c))
+    if qkv_heads:
+        B, N, H, d = qkv_heads
+        params.update(layout=1, batch=B, seq_len=N, heads=H, head_dim=d)
+    return LinearWorkload(name, np.ascontiguousarray(x), np.ascontiguousarray(w), params)
+
+
+# ViT-B projections at the headline batch: Q/K/V (head-split) and the output one
+LINEAR_CONFIGS = {
+    "vitb_qkv_b128_n197_c768": dict(rows=128 * 197, in_features=768, out_features=3 * 768,
+                                     qkv_heads=(128, 197, 12, 64)),
+    "vitb_proj_b128_n197_c768": dict(rows=128 * 197, in_features=768, out_features=768),
+}
+
+
+def linear_workload(name: str, seed: int = 2000) -> LinearWorkload:
+    spec = dict(LINEAR_CONFIGS[name])
+    return make_linear(seed=seed, name=name, **spec)

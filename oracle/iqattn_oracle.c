@@ -230,3 +230,21 @@ int orc_forward(const orc_params* p, const int8_t* q, const int8_t* k,
   free(lrow); free(erow); free(prow); free(crow); free(wrow);
   return rc;
 }
+
+/* Linear layer: integer product over the input features, then the same dyadic
+ * requantisation as the attention's (R10, R11, R12).  Plain loops, int64. */
+int orc_linear(const int8_t* x, const int8_t* w, int64_t rows, int64_t in_features,
+               int64_t out_features, int32_t b, int32_t c, int8_t* out, int64_t row_begin,
+               int64_t row_end) {
+  if (rows < 0 || in_features < 1 || out_features < 1 || b < 1 || c < 0 || c > 62 ||
+      row_begin < 0 || row_end > rows || row_begin > row_end)
+    return -1;
+  for (int64_t m = row_begin; m < row_end; ++m)
+    for (int64_t n = 0; n < out_features; ++n) {
+      int64_t acc = 0;
+      for (int64_t k = 0; k < in_features; ++k)
+        acc += (int64_t)x[m * in_features + k] * (int64_t)w[n * in_features + k];
+      out[m * out_features + n] = (int8_t)orc_requant(acc, b, c);
+    }
+  return 0;
+}

@@ -78,6 +78,16 @@ int orc_forward(const orc_params* p, const int8_t* q, const int8_t* k,
                 const int8_t* v, int8_t* out, int64_t head_begin,
                 int64_t head_end, const orc_dump* dump);
 
+/* Integer-only linear layer (I-ViT sec. 3.2 applied to a projection):
+ *   out[m][n] = clip(floor(b * sum_k x[m][k] * w[n][k] / 2^c), -127, 127)
+ * for rows [row_begin, row_end); x is [rows][in] and w is [out][in] int8,
+ * row-major; out is [rows][out] (only the given rows are written).  No bias
+ * term: the pages give the dyadic product alone.  Returns 0, or -1 for
+ * out-of-range arguments.                                                    */
+int orc_linear(const int8_t* x, const int8_t* w, int64_t rows, int64_t in_features,
+               int64_t out_features, int32_t b, int32_t c, int8_t* out, int64_t row_begin,
+               int64_t row_end);
+
 /* Steps exposed one at a time for the tests. */
 int32_t orc_requant(int64_t x, int32_t b, int32_t c);
 void    orc_requant_array(const int64_t* x, int64_t n, int32_t b, int32_t c,

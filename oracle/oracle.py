@@ -58,6 +58,9 @@ def _load():
         lib.orc_forward.argtypes = [C.POINTER(_Params), C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_int64, C.c_int64, C.POINTER(_Dump)]
         lib.orc_requant.argtypes = [C.c_int64, C.c_int32, C.c_int32]
+        lib.orc_linear.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                   C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int64]
+        lib.orc_linear.restype = C.c_int
         lib.orc_requant.restype = C.c_int32
         lib.orc_requant_array.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
                                           C.c_void_p]
@@ -169,3 +172,22 @@ def shift_exp(delta: int, i0: int, n: int) -> int:
 
 def ilog2r(x: int) -> int:
     return int(_load().orc_ilog2r(int(x)))
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: int, c: int, rows=None) -> np.ndarray:
+    """Integer-only linear layer: x [rows, in] int8, w [out, in] int8 ->
+    [rows, out] int8 (or [r1 - r0, out] for rows=(r0, r1))."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    M, K = x.shape
+    Nc, K2 = w.shape
+    if K != K2:
+        raise ValueError("x and w disagree on in_features")
+    r0, r1 = (0, M) if rows is None else rows
+    out = np.zeros((M, Nc), dtype=np.int8)
+    rc = lib.orc_linear(x.ctypes.data, w.ctypes.data, M, K, Nc, int(b), int(c),
+                        out.ctypes.data, r0, r1)
+    if rc != 0:
+        raise ValueError(f"orc_linear: invalid arguments ({rc})")
+    return out[r0:r1]

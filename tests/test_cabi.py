@@ -19,7 +19,7 @@ def _declared_functions():
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(iqattn_\w+)\s*\(", text))
+            names |= set(re.findall(r"\b(iq(?:attn|linear)_\w+)\s*\(", text))
     return names
 
 
@@ -44,6 +44,10 @@ def test_header_constants_match_binding():
                  "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
                  "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_LIS_VALU", "IQATTN_LIS_MFMA",
                  "IQATTN_MAX_SEQ"):
+        m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(IQ, name), name
+    text = open(os.path.join(ROOT, "include", "iqlinear.h")).read()
+    for name in ("IQLINEAR_PLAIN", "IQLINEAR_QKV_HEADS"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(IQ, name), name
 
@@ -98,3 +102,40 @@ def test_strerror_texts(lib):
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         s = IQ.iqattn_strerror(code)
         assert isinstance(s, str) and s
+
+
+def _linear_rc(lib, **over):
+    p = dict(rows=4, in_features=64, out_features=64, layout=IQ.IQLINEAR_PLAIN, batch=0,
+             seq_len=0, heads=0, head_dim=0, b=(20000, 1, 1), c=(20, 1, 1))
+    p.update(over)
+    s = IQ.make_linear_params(p)
+    ctx = C.c_void_p(12345)
+    rc = lib.iqlinear_create(C.byref(s), C.byref(ctx))
+    return rc, ctx.value
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(rows=-1), IQ.IQATTN_E_SHAPE),
+    (dict(in_features=48), IQ.IQATTN_E_SHAPE),
+    (dict(in_features=0), IQ.IQATTN_E_SHAPE),
+    (dict(out_features=72), IQ.IQATTN_E_SHAPE),
+    (dict(layout=2), IQ.IQATTN_E_INVAL),
+    (dict(b=(0, 1, 1)), IQ.IQATTN_E_INVAL),
+    (dict(c=(63, 1, 1)), IQ.IQATTN_E_INVAL),
+    (dict(layout=IQ.IQLINEAR_QKV_HEADS, rows=6, out_features=192, batch=2, seq_len=3, heads=1,
+          head_dim=64, b=(1, 1, 0), c=(1, 1, 1)), IQ.IQATTN_E_INVAL),
+    (dict(layout=IQ.IQLINEAR_QKV_HEADS, rows=7, out_features=192, batch=2, seq_len=3, heads=1,
+          head_dim=64, b=(1, 1, 1), c=(1, 1, 1)), IQ.IQATTN_E_SHAPE),
+    (dict(layout=IQ.IQLINEAR_QKV_HEADS, rows=6, out_features=24, batch=2, seq_len=3, heads=1,
+          head_dim=8, b=(1, 1, 1), c=(1, 1, 1)), IQ.IQATTN_E_SHAPE),
+])
+def test_linear_create_rejects_bad_parameters_before_any_device_call(lib, over, code):
+    rc, ctx = _linear_rc(lib, **over)
+    assert rc == code
+    assert ctx is None
+
+
+def test_linear_null_arguments(lib):
+    assert lib.iqlinear_create(None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqlinear_destroy(None) == IQ.IQATTN_OK
+    assert lib.iqlinear_forward(None, None, None, None, None, None, None) == IQ.IQATTN_E_NULL

@@ -1,0 +1,116 @@
+"""Bit-exact parity of the int8 linear layer (through the C-ABI) with the
+CPU oracle: plain and head-split layouts, ragged row counts, half-width column
+tiles, extreme dyadic pairs, and the ViT-B projection shapes (sampled rows)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from integer_only_quantized_int8_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "no GPU visible"
+    return torch
+
+
+def run_gpu(torch, lw, params=None):
+    from integer_only_quantized_int8_amd.iqattn import IQLinear
+    P = lw.params if params is None else params
+    lin = IQLinear(P)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(lw.x).to(dev)
+    w = torch.from_numpy(lw.w).to(dev)
+    if P["layout"] == 1:
+        shape = (P["batch"], P["heads"], P["seq_len"], P["head_dim"])
+        outs = tuple(torch.full(shape, 99, dtype=torch.int8, device=dev) for _ in range(3))
+        lin.forward(x, w, outs)
+        torch.cuda.synchronize()
+        res = [o.cpu().numpy() for o in outs]
+    else:
+        out = torch.full((P["rows"], P["out_features"]), 99, dtype=torch.int8, device=dev)
+        lin.forward(x, w, out)
+        torch.cuda.synchronize()
+        res = out.cpu().numpy()
+    lin.close()
+    return res
+
+
+def oracle_rows(lw, rows, params=None):
+    """Oracle result of the given rows: [len(rows), out] per (b, c) pair."""
+    P = lw.params if params is None else params
+    res = []
+    for r in rows:
+        if P["layout"] == 1:
+            C3 = P["out_features"] // 3
+            parts = [oracle.linear(lw.x[r:r + 1], lw.w[i * C3:(i + 1) * C3], P["b"][i], P["c"][i])[0]
+                     for i in range(3)]
+            res.append(np.concatenate(parts))
+        else:
+            res.append(oracle.linear(lw.x[r:r + 1], lw.w, P["b"][0], P["c"][0])[0])
+    return np.stack(res)
+
+
+def check(torch, lw, rows=None, params=None, label=""):
+    P = lw.params if params is None else params
+    _say(f"[linear] {label} rows={P['rows']} in={P['in_features']} out={P['out_features']} "
+         f"layout={P['layout']}")
+    got = run_gpu(torch, lw, P)
+    M = P["rows"]
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    ref = oracle_rows(lw, sel, P)
+    if P["layout"] == 1:
+        B, N, H, d = P["batch"], P["seq_len"], P["heads"], P["head_dim"]
+        for which in range(3):
+            g = got[which].transpose(0, 2, 1, 3).reshape(B * N, H * d)[sel]
+            r = ref[:, which * H * d:(which + 1) * H * d]
+            if not np.array_equal(g, r):
+                bad = np.argwhere(g != r)
+                raise AssertionError(f"{label}: tensor {which} differs at {len(bad)} entries, "
+                                     f"first {bad[:4].tolist()}")
+    else:
+        g = got[sel]
+        if not np.array_equal(g, ref):
+            bad = np.argwhere(g != ref)
+            raise AssertionError(f"{label}: {len(bad)} entries differ, first {bad[:4].tolist()}")
+
+
+@pytest.mark.parametrize("rows,fin,fout", [
+    (1, 64, 64), (128, 64, 128), (129, 128, 64), (300, 192, 192), (64, 768, 320),
+    (257, 256, 128), (5, 64, 1024), (33, 64, 48), (130, 128, 208),
+])
+def test_linear_plain_shapes(torch_dev, rows, fin, fout):
+    lw = W.make_linear(rows, fin, fout, seed=rows + fin + fout)
+    check(torch_dev, lw, label=f"plain {rows}x{fin}x{fout}")
+
+
+@pytest.mark.parametrize("B,N,H,d", [(1, 197, 3, 64), (2, 49, 3, 32), (3, 50, 2, 64), (1, 7, 1, 64)])
+def test_linear_qkv_head_split(torch_dev, B, N, H, d):
+    lw = W.make_linear(B * N, 128, 3 * H * d, seed=B * 100 + N, qkv_heads=(B, N, H, d))
+    check(torch_dev, lw, label=f"qkv B{B} N{N} H{H} d{d}")
+
+
+def test_linear_extreme_dyadic_pairs(torch_dev):
+    lw = W.make_linear(70, 128, 64, seed=3, sigma_x=127.0, sigma_w=127.0)
+    for b, c in ((1, 0), ((1 << 31) - 1, 62), ((1 << 31) - 1, 40), ((1 << 15) - 1, 32),
+                 (1 << 14, 1), (3, 12)):
+        check(torch_dev, lw, params=dict(lw.params, b=(b,), c=(c,)), label=f"b={b} c={c}")
+
+
+def test_linear_vitb_projections_sampled_rows(torch_dev):
+    for name in W.LINEAR_CONFIGS:
+        lw = W.linear_workload(name)
+        M = lw.params["rows"]
+        rows = sorted(set([0, 1, 127, 128, M - 1] +
+                          list(np.random.default_rng(1).choice(M, 24, replace=False))))
+        check(torch_dev, lw, rows=rows, label=name)
