@@ -92,6 +92,63 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str) -> dict:
     return rec
 
 
+def bench_linear(args):
+    """Time one int8 linear layer (x W^T with the fused requantisation) on the
+    ViT-B projection shapes; roofline against the dense int8 MFMA peak."""
+    import numpy as np
+    import torch
+    from integer_only_quantized_int8_amd import workloads as W
+    from integer_only_quantized_int8_amd.iqattn import IQLinear
+    lw = W.linear_workload(args.linear)
+    P = lw.params
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(lw.x).to(dev)
+    w = torch.from_numpy(lw.w).to(dev)
+    lin = IQLinear(P)
+    outs = None
+    if P["layout"] == 1:
+        shape = (P["batch"], P["heads"], P["seq_len"], P["head_dim"])
+        outs = tuple(torch.empty(shape, dtype=torch.int8, device=dev) for _ in range(3))
+    else:
+        outs = torch.empty((P["rows"], P["out_features"]), dtype=torch.int8, device=dev)
+    for _ in range(args.warmup):
+        lin.forward(x, w, outs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            lin.forward(x, w, outs)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = g0.elapsed_time(g1) / args.steps
+    M, K, Nc = P["rows"], P["in_features"], P["out_features"]
+    ops = 2.0 * M * K * Nc
+    tops = ops / (step_ms * 1e-3) / 1e12
+    ktops = ops / (kern_ms * 1e-3) / 1e12
+    hbm = float(M * K + Nc * K + M * Nc)
+    res = {"metric": f"integer-only int8 linear TOPS, {lw.name}", "value": round(tops, 2),
+           "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int8", "data": "synthetic (seeded int8 x and w)",
+           "config": {"workload": lw.name, "rows": M, "in_features": K, "out_features": Nc,
+                      "layout": "qkv_heads" if P["layout"] == 1 else "plain"},
+           "kernel_us_mean": round(kern_ms * 1e3, 3),
+           "roofline": {"bound": "mfma", "achieved": round(ktops, 1), "peak": MFMA_I8_PEAK_TOPS,
+                        "unit": "TFLOP/s", "frac": round(ktops / MFMA_I8_PEAK_TOPS, 4),
+                        "traffic": None, "algorithmic_bytes_per_launch": int(hbm),
+                        "hbm_gbs_at_algorithmic_bytes": round(hbm / (kern_ms * 1e-3) / 1e9, 1)}}
+    lin.close()
+    print(json.dumps(res), flush=True)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -113,6 +170,9 @@ def main():
                     help="heads timed on the CPU oracle (0 = all heads, at most ~30 s)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--linear", default=None,
+                    help="time an int8 linear layer instead (workload name from "
+                         "workloads.LINEAR_CONFIGS, e.g. vitb_qkv_b128_n197_c768)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter files and exit (no GPU use)")
@@ -139,6 +199,10 @@ def main():
     import torch
     from integer_only_quantized_int8_amd import workloads as W
     from integer_only_quantized_int8_amd.iqattn import IQAttn
+
+    if args.linear:
+        bench_linear(args)
+        return
 
     t0 = time.time()
     w = W.config_workload(args.config)

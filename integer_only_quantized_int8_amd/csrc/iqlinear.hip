@@ -5,13 +5,14 @@
 // Linear Operations" (integer product, then (b * acc) >> c to int8); sec. 3.1
 // (the MSA projections).
 //
-// Kernel: one workgroup of 4 waves computes a 128 (rows) x 128 (output
+// Kernel: a workgroup of 2 x 2 waves computes a 128 (rows) x 128 (output
 // columns) tile as Y^T = W . X^T with v_mfma_i32_16x16x64_i8, so a lane ends
 // with 4 adjacent output columns of one row (one 4-byte store).  Each wave owns
-// a 64 x 64 quarter: 4 x 4 MFMA tiles, 64 accumulator VGPRs.  The k loop steps
-// by 64 bytes: the next step's X and W tiles (2 x 8 KB) are loaded into
-// registers while the current step runs from LDS, then written to the other
-// LDS buffer (double buffering, one barrier per step).  LDS rows are 64 bytes
+// 64 x 64: 4 x 4 MFMA tiles, 64 accumulator registers (larger wave tiles need
+// so many registers that one wave per SIMD remains, which measured slower).
+// The k loop steps by 64 bytes: the next step's X and W tiles (2 x 8 KB) are
+// loaded into registers while the current step runs from LDS, then written to
+// the other LDS buffer (double buffering, one barrier per step).  LDS rows are 64 bytes
 // with the 16-byte chunks XOR-swizzled by (row >> 1) & 3, which makes the
 // b128 operand reads of 16 rows x 4 chunks bank-conflict free.
 #include "iqattn_dev.h"
@@ -24,7 +25,6 @@
 namespace iqattn {
 namespace {
 
-constexpr int kTile = 128;  // rows and output columns per workgroup
 constexpr int kStep = 64;   // k bytes per step
 
 struct LinParams {
@@ -39,57 +39,59 @@ struct LinParams {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
 
-__global__ __launch_bounds__(256) void iqlinear_gemm(LinParams p) {
-  __shared__ __attribute__((aligned(16))) int8_t sX[2][kTile * kStep];
-  __shared__ __attribute__((aligned(16))) int8_t sW[2][kTile * kStep];
+// Workgroup of WM x WN waves; each wave owns TM x TN MFMA tiles (16 x 16) of
+// rows x output columns, so the workgroup tile is (16 WM TM) x (16 WN TN).
+template <int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(64 * WM * WN) void iqlinear_gemm(LinParams p) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;   // workgroup tile
+  constexpr int XCH = BM * 4 / NT, WCH = BN * 4 / NT;   // 16-byte chunks per thread per step
+  static_assert(BM * 4 % NT == 0 && BN * 4 % NT == 0, "tile / thread mismatch");
+  __shared__ __attribute__((aligned(16))) int8_t sX[2][BM * kStep];
+  __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * kStep];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;  // wave quarter: rows 64 wm.., columns 64 wn..
-  const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;
+  const int wm = wave % WM, wn = wave / WM;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
 
-  // global tile loads: 128 rows x 4 chunks of 16 bytes per operand, two
-  // chunks per thread; rows past the end read as zeros (buffer range)
+  // global tile loads (rows past the end read as zeros: buffer range)
   const __amdgpu_buffer_rsrc_t xr = buf_rsrc(p.x, (uint32_t)(p.rows * p.in_f));
-  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(p.w, (uint32_t)(p.out_f * p.in_f));  // rows >= out: 0
-  int lrow[2], lch[2];
+  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(p.w, (uint32_t)(p.out_f * p.in_f));
+  int xoff[XCH], xls[XCH], woff[WCH], wls[WCH];
+  bool xin[XCH];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i;
-    lrow[i] = idx >> 2;
-    lch[i] = idx & 3;
+  for (int i = 0; i < XCH; ++i) {
+    const int idx = tid + NT * i, row = idx >> 2, ch = idx & 3;
+    xin[i] = m0 + row < p.rows;
+    xoff[i] = (xin[i] ? m0 + row : 0) * p.in_f + 16 * ch;
+    xls[i] = swz(row, ch);
   }
-  // byte offsets of this thread's chunks in X (rows m0 + lrow) and W (rows n0 + lrow)
-  int xoff[2], woff[2];
-  bool xin[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = m0 + lrow[i];
-    xin[i] = m < p.rows;
-    xoff[i] = (xin[i] ? m : 0) * p.in_f + 16 * lch[i];
-    woff[i] = (n0 + lrow[i]) * p.in_f + 16 * lch[i];
+  for (int i = 0; i < WCH; ++i) {
+    const int idx = tid + NT * i, row = idx >> 2, ch = idx & 3;
+    woff[i] = (n0 + row) * p.in_f + 16 * ch;
+    wls[i] = swz(row, ch);
   }
-  v4i xv[2], wv[2];
+  v4i xv[XCH], wv[WCH];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i] + k0, 0, 0);
-      wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[i] + k0, 0, 0);
-    }
+    for (int i = 0; i < XCH; ++i) xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i] + k0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[i] + k0, 0, 0);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(v4i*)(sX[buf] + swz(lrow[i], lch[i])) = xin[i] ? xv[i] : v4i{0, 0, 0, 0};
-      *(v4i*)(sW[buf] + swz(lrow[i], lch[i])) = wv[i];
-    }
+    for (int i = 0; i < XCH; ++i) *(v4i*)(sX[buf] + xls[i]) = xin[i] ? xv[i] : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) *(v4i*)(sW[buf] + wls[i]) = wv[i];
   };
 
-  v4i acc[4][4];  // [n tile][m tile]
+  v4i acc[TN][TM];  // [n tile][m tile]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    for (int b = 0; b < TM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
 
   const int nks = p.in_f / kStep;
   gload(0);
@@ -98,29 +100,28 @@ __global__ __launch_bounds__(256) void iqlinear_gemm(LinParams p) {
   for (int ks = 0; ks < nks; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < nks) gload((ks + 1) * kStep);
-    v4i af[4], bf[4];
+    v4i bf[TM];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      af[t] = *(const v4i*)(sW[buf] + swz(64 * wn + 16 * t + li, g));  // W rows = output columns
-      bf[t] = *(const v4i*)(sX[buf] + swz(64 * wm + 16 * t + li, g));  // X rows
+    for (int t = 0; t < TM; ++t) bf[t] = *(const v4i*)(sX[buf] + swz(16 * (TM * wm + t) + li, g));
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+      const v4i af = *(const v4i*)(sW[buf] + swz(16 * (TN * wn + a) + li, g));  // output columns
+#pragma unroll
+      for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(af, bf[b], acc[a][b]);
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma64(af[a], bf[b], acc[a][b]);
     if (ks + 1 < nks) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds output columns n0 + 64 wn + 16 a + 4 g + r of row
-  // m0 + 64 wm + 16 b + li
+  // epilogue: lane holds output columns n0 + 16 (TN wn + a) + 4 g + r of row
+  // m0 + 16 (TM wm + b) + li
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int m = m0 + 64 * wm + 16 * b + li;
+  for (int b = 0; b < TM; ++b) {
+    const int m = m0 + 16 * (TM * wm + b) + li;
     if (m >= p.rows) continue;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int n = n0 + 64 * wn + 16 * a + 4 * g;
+    for (int a = 0; a < TN; ++a) {
+      const int n = n0 + 16 * (TN * wn + a) + 4 * g;
       if (n >= p.out_f) continue;  // out is a multiple of 16: the whole 16-column tile
       int which = 0, col = n;
       if (p.layout == IQLINEAR_QKV_HEADS) {
@@ -148,6 +149,14 @@ __global__ __launch_bounds__(256) void iqlinear_gemm(LinParams p) {
     }
   }
 }
+
+#ifndef IQLINEAR_CFG
+#define IQLINEAR_CFG 2, 2, 4, 4
+#endif
+constexpr int kCfg[4] = {IQLINEAR_CFG};
+#define IQLINEAR_KERNEL iqlinear_gemm<kCfg[0], kCfg[1], kCfg[2], kCfg[3]>
+constexpr int kBM = 16 * kCfg[0] * kCfg[2], kBN = 16 * kCfg[1] * kCfg[3];
+constexpr int kNT = 64 * kCfg[0] * kCfg[1];
 
 }  // namespace
 }  // namespace iqattn
@@ -228,8 +237,8 @@ extern "C" int iqlinear_forward(iqlinear_ctx* c, const int8_t* x, const int8_t* 
   lp.out[0] = out0;
   lp.out[1] = qkv ? out1 : out0;
   lp.out[2] = qkv ? out2 : out0;
-  const dim3 grid((unsigned)((lp.rows + kTile - 1) / kTile), (unsigned)(lp.out_f / kTile + (lp.out_f % kTile ? 1 : 0)));
-  hipLaunchKernelGGL(iqlinear_gemm, grid, dim3(256), 0, (hipStream_t)hip_stream, lp);
+  const dim3 grid((unsigned)((lp.rows + kBM - 1) / kBM), (unsigned)((lp.out_f + kBN - 1) / kBN));
+  hipLaunchKernelGGL(IQLINEAR_KERNEL, grid, dim3(kNT), 0, (hipStream_t)hip_stream, lp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqlinear launch");
   return IQATTN_OK;
