@@ -233,3 +233,83 @@ LINEAR_CONFIGS = {
 def linear_workload(name: str, seed: int = 2000) -> LinearWorkload:
     spec = dict(LINEAR_CONFIGS[name])
     return make_linear(seed=seed, name=name, **spec)
+
+
+# ---------------------------------------------------------------- ShiftGELU / I-LayerNorm
+S_G, S_GPARAMS, S_LNX, S_LNMU, S_LNSIG, S_GAMMA, S_BETA, S_LNPARAMS = 11, 12, 13, 14, 15, 16, 17, 18
+
+
+@dataclass
+class GeluWorkload:
+    """int8 input of the MLP's GELU, x [rows, cols], plus its parameters."""
+    name: str
+    rows: int
+    cols: int
+    x: np.ndarray
+    params: Dict[str, int] = field(default_factory=dict)
+
+
+def gelu_params(seed: int) -> Dict[str, int]:
+    """Input scale 1/16 (I0 = 16), 22 extra exponent fraction bits, M = 40,
+    k_out = 8; output pair b uniform in [2^14, 2^15), c = 22: b / 2^c in
+    [1/256, 1/128) maps x * sigma (scale 1/(16 * 128)) to an output scale in
+    (1/16, 1/8], wide enough for the largest input, 127/16."""
+    b = Stream(seed, S_GPARAMS).randint(1 << 14, (1 << 15) - 1, 1)
+    return dict(i0=16, exp_frac_bits=22, intdiv_m=40, k_out=8, b=int(b[0]), c=22)
+
+
+def make_gelu(rows: int, cols: int, seed: int, sigma=32.0, name: str = "custom") -> GeluWorkload:
+    x = int8_gaussian(Stream(seed, S_G), (rows, cols), sigma)
+    return GeluWorkload(name, rows, cols, x, gelu_params(seed))
+
+
+@dataclass
+class LayerNormWorkload:
+    """int8 input of a LayerNorm, x [rows, cols], int8 gamma and int32 beta per
+    column, plus its parameters."""
+    name: str
+    rows: int
+    cols: int
+    x: np.ndarray
+    gamma: np.ndarray
+    beta: np.ndarray
+    params: Dict[str, int] = field(default_factory=dict)
+
+
+def layernorm_params(seed: int) -> Dict[str, int]:
+    """7 fraction bits on the normalised value, M = 23 for floor(2^M / sd);
+    output pair b uniform in [2^14, 2^15), c = 22."""
+    b = Stream(seed, S_LNPARAMS).randint(1 << 14, (1 << 15) - 1, 1)
+    return dict(norm_frac_bits=7, intdiv_m=23, b=int(b[0]), c=22)
+
+
+def make_layernorm(rows: int, cols: int, seed: int, name: str = "custom",
+                   mu_sigma=12.0, sigma_range=(8.0, 40.0), gamma_sigma=48.0,
+                   beta_range=1 << 14) -> LayerNormWorkload:
+    """LayerNorm inputs with inter-channel variation: column j has its own mean
+    mu_j ~ N(0, mu_sigma) and spread sigma_j uniform in sigma_range; element
+    x[m, j] = clip(round(mu_j + sigma_j * z), -127, 127).  gamma is int8
+    N(0, gamma_sigma), beta uniform in [-beta_range, beta_range]."""
+    mu = mu_sigma * Stream(seed, S_LNMU).normal(cols)
+    lo, hi = sigma_range
+    sg = lo + (hi - lo) * Stream(seed, S_LNSIG).uniform_co(cols)
+    z = Stream(seed, S_LNX).normal(rows * cols).reshape(rows, cols)
+    x = np.clip(_round_half_away(mu[None, :] + sg[None, :] * z), -127, 127).astype(np.int8)
+    gamma = int8_gaussian(Stream(seed, S_GAMMA), (cols,), gamma_sigma)
+    beta = Stream(seed, S_BETA).randint(-beta_range, beta_range, cols).astype(np.int32)
+    return LayerNormWorkload(name, rows, cols, x, gamma, beta, layernorm_params(seed))
+
+
+# ViT-B/16 at 224 px, batch 128: 197 tokens, hidden 768, MLP 3072.
+GELU_CONFIGS = {"vitb_mlp_b128_n197_c3072": (128 * 197, 3072)}
+LAYERNORM_CONFIGS = {"vitb_ln_b128_n197_c768": (128 * 197, 768)}
+
+
+def gelu_workload(name: str, seed: int = 3000) -> GeluWorkload:
+    rows, cols = GELU_CONFIGS[name]
+    return make_gelu(rows, cols, seed, name=name)
+
+
+def layernorm_workload(name: str, seed: int = 4000) -> LayerNormWorkload:
+    rows, cols = LAYERNORM_CONFIGS[name]
+    return make_layernorm(rows, cols, seed, name=name)

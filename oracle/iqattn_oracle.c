@@ -248,3 +248,110 @@ int orc_linear(const int8_t* x, const int8_t* w, int64_t rows, int64_t in_featur
     }
   return 0;
 }
+
+/* ---------------------------------------------------------------- ShiftGELU
+ * G1  The max is taken over the row (the last axis, as the softmax's), and
+ *     clamped at 0 so that both exponents, Ip - Imax and -Imax, are <= 0: the
+ *     shift-based 2^x of sec. 3.3 is defined for non-positive arguments only.
+ * G2  sigma = e1 / (e1 + e2) by the IntDiv of sec. 3.3 with k_out output bits;
+ *     sigma reaches 2^(k_out - 1) only when e2 = 0 and is clamped below it (R9).
+ *     A zero numerator (e1 = 0: Ip far below Imax) gives sigma = 0; the
+ *     division is then not taken, since e1 + e2 can be 0 as well when Imax is
+ *     large enough that 2^x of -Imax underflows.
+ * G3  The product x * sigma is requantised to int8 by a dyadic pair (sec. 3.2),
+ *     as every integer operator's output is.                                 */
+int orc_shiftgelu(const int8_t* x, int64_t rows, int64_t cols, int32_t i0, int32_t exp_frac_bits,
+                  int32_t intdiv_m, int32_t k_out, int32_t b, int32_t c, int8_t* out,
+                  int64_t row_begin, int64_t row_end, int64_t* dump) {
+  if (rows < 0 || cols < 1 || i0 < 1 || i0 > 32768 || exp_frac_bits < 0 || exp_frac_bits > 30 ||
+      k_out < 2 || k_out > 8 ||
+      intdiv_m < k_out - 1 || intdiv_m > 40 || b < 1 || c < 0 || c > 62 || row_begin < 0 ||
+      row_end > rows || row_begin > row_end)
+    return -1;
+  int64_t* ip = (int64_t*)malloc((size_t)cols * sizeof(int64_t));
+  if (!ip) return -1;
+  const int64_t pmax = pow2(k_out - 1) - 1;
+  for (int64_t m = row_begin; m < row_end; ++m) {
+    int64_t imax = 0; /* G1: clamped at 0 */
+    for (int64_t j = 0; j < cols; ++j) {
+      const int64_t v = x[m * cols + j];
+      ip[j] = v + floor_div(v, 2) + floor_div(v, 8) + floor_div(v, 16); /* 1.1011b */
+      if (ip[j] > imax) imax = ip[j];
+    }
+    for (int64_t j = 0; j < cols; ++j) {
+      const int64_t e1 = orc_shift_exp((int32_t)(ip[j] - imax), i0, exp_frac_bits);
+      const int64_t e2 = orc_shift_exp((int32_t)(-imax), i0, exp_frac_bits);
+      int64_t sig = 0; /* G2: e1 = 0 gives 0 */
+      if (e1 > 0) {
+        const int64_t f = floor_div(pow2(intdiv_m), e1 + e2);
+        sig = floor_div(f * e1, pow2(intdiv_m - (k_out - 1)));
+        if (sig > pmax) sig = pmax;
+      }
+      if (dump) {
+        int64_t* dj = dump + (m * cols + j) * 4;
+        dj[0] = ip[j];
+        dj[1] = e1;
+        dj[2] = e2;
+        dj[3] = sig;
+      }
+      out[m * cols + j] = (int8_t)orc_requant((int64_t)x[m * cols + j] * sig, b, c); /* G3 */
+    }
+  }
+  free(ip);
+  return 0;
+}
+
+/* ---------------------------------------------------------------- I-LayerNorm */
+static int64_t bit_length(int64_t v) {
+  int64_t n = 0;
+  while (v > 0) { ++n; v >>= 1; }
+  return n;
+}
+
+int64_t orc_isqrt10(int64_t v) {
+  if (v <= 0) return 0;
+  int64_t r = pow2(bit_length(v) / 2);
+  for (int it = 0; it < 10; ++it) r = floor_div(r + floor_div(v, r), 2);
+  return r;
+}
+
+/* L1  mean = floor(sum / cols) (integer division rounding down).
+ * L2  var = floor(sum of squared deviations / cols); the square root by the
+ *     page's ten fixed Newton steps; a zero deviation (constant row) takes
+ *     sd = 1 so that the division is defined (every n is then 0).
+ * L3  The division by sd is the IntDiv of sec. 3.3 with constant M: n keeps
+ *     F fraction bits, n = (xc * floor(2^M / sd)) >> (M - F).
+ * L4  gamma is int8, beta int32 at the scale of n * gamma; the affine result
+ *     is requantised to int8 by a dyadic pair (sec. 3.2).                    */
+int orc_ilayernorm(const int8_t* x, const int8_t* gamma, const int32_t* beta, int64_t rows,
+                   int64_t cols, int32_t norm_frac_bits, int32_t intdiv_m, int32_t b, int32_t c,
+                   int8_t* out, int64_t row_begin, int64_t row_end, int64_t* stat_dump) {
+  if (rows < 0 || cols < 1 || norm_frac_bits < 0 || intdiv_m < norm_frac_bits ||
+      intdiv_m > 40 || b < 1 || c < 0 || c > 62 || row_begin < 0 || row_end > rows ||
+      row_begin > row_end)
+    return -1;
+  for (int64_t m = row_begin; m < row_end; ++m) {
+    const int8_t* xr = x + m * cols;
+    int64_t sum = 0;
+    for (int64_t j = 0; j < cols; ++j) sum += xr[j];
+    const int64_t mean = floor_div(sum, cols);
+    int64_t sq = 0;
+    for (int64_t j = 0; j < cols; ++j) sq += (xr[j] - mean) * (xr[j] - mean);
+    const int64_t var = floor_div(sq, cols);
+    int64_t sd = orc_isqrt10(var);
+    if (sd == 0) sd = 1;
+    const int64_t fs = floor_div(pow2(intdiv_m), sd);
+    if (stat_dump) {
+      stat_dump[m * 4 + 0] = mean;
+      stat_dump[m * 4 + 1] = var;
+      stat_dump[m * 4 + 2] = sd;
+      stat_dump[m * 4 + 3] = fs;
+    }
+    for (int64_t j = 0; j < cols; ++j) {
+      const int64_t n = floor_div((xr[j] - mean) * fs, pow2(intdiv_m - norm_frac_bits));
+      const int64_t y = n * gamma[j] + beta[j];
+      out[m * cols + j] = (int8_t)orc_requant(y, b, c);
+    }
+  }
+  return 0;
+}

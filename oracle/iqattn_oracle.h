@@ -25,8 +25,13 @@
  *     plus the next lower bit;  sec. V, requantisation module (Eq. 12):
  *     b and c positive integers.
  *
+ *   I-ViT sec. 3.4 "Integer-only GELU: ShiftGELU" and sec. 3.5 "Integer-only
+ *     LayerNorm: I-LayerNorm" for the two element-wise/row-wise operators
+ *     around the attention (orc_shiftgelu, orc_ilayernorm).
+ *
  * Readings taken where the pages are silent, garbled or ambiguous are listed
- * next to the code that takes them (R1..R22 in the comments of the .c file).
+ * next to the code that takes them (R1..R22, G1..G3, L1..L4 in the comments of
+ * the .c file).
  * Parity unpinned: the readings themselves (I0 = 1/S_logit, the extra exponent
  * fraction bits n, M, the clamp of P at 2^(k_out-1)-1, floor requantisation,
  * bias added to the int32 accumulator, the midpoint of the log2 rounding, the
@@ -87,6 +92,37 @@ int orc_forward(const orc_params* p, const int8_t* q, const int8_t* k,
 int orc_linear(const int8_t* x, const int8_t* w, int64_t rows, int64_t in_features,
                int64_t out_features, int32_t b, int32_t c, int8_t* out, int64_t row_begin,
                int64_t row_end);
+
+/* ShiftGELU (I-ViT sec. 3.4) on x [rows][cols] int8 at scale 1/i0:
+ *   Ip   = x + (x >> 1) + (x >> 3) + (x >> 4)        1.702 ~ 1.1011b
+ *   Imax = max(0, max over the row of Ip)            (G1)
+ *   e1   = shift_exp(Ip - Imax), e2 = shift_exp(-Imax)   (Shiftmax's 2^x)
+ *   sig  = min((floor(2^M / (e1 + e2)) * e1) >> (M - (k_out - 1)),
+ *              2^(k_out - 1) - 1), 0 when e1 = 0     (G2, R9)
+ *   out  = clip((b * (x * sig)) >> c, -127, 127)     (G3)
+ * Rows [row_begin, row_end) are written; dump, when not NULL, receives
+ * (Ip, e1, e2, sig) per element [rows][cols][4].  Returns 0 or -1 (bad
+ * arguments).                                                                */
+int orc_shiftgelu(const int8_t* x, int64_t rows, int64_t cols, int32_t i0, int32_t exp_frac_bits,
+                  int32_t intdiv_m, int32_t k_out, int32_t b, int32_t c, int8_t* out,
+                  int64_t row_begin, int64_t row_end, int64_t* dump);
+
+/* Integer square root of I-LayerNorm (I-ViT sec. 3.5): ten iterations of
+ * I <- (I + floor(v / I)) >> 1 from I = 2^floor(bits(v) / 2), bits(v) the
+ * bit length of v; v = 0 gives 0.                                            */
+int64_t orc_isqrt10(int64_t v);
+
+/* I-LayerNorm (I-ViT sec. 3.5) on x [rows][cols] int8 with per-column gamma
+ * (int8) and beta (int32):
+ *   mean = floor(sum x / cols); xc = x - mean                 (L1)
+ *   var  = floor(sum xc^2 / cols); sd = isqrt10(var), 0 -> 1   (L2)
+ *   n    = (xc * floor(2^M / sd)) >> (M - F)                   (L3)
+ *   out  = clip((b * (n * gamma + beta)) >> c, -127, 127)      (L4)
+ * Rows [row_begin, row_end) are written; stat_dump, when not NULL, receives
+ * (mean, var, sd, floor(2^M / sd)) per row [rows][4].  Returns 0 or -1.      */
+int orc_ilayernorm(const int8_t* x, const int8_t* gamma, const int32_t* beta, int64_t rows,
+                   int64_t cols, int32_t norm_frac_bits, int32_t intdiv_m, int32_t b, int32_t c,
+                   int8_t* out, int64_t row_begin, int64_t row_end, int64_t* stat_dump);
 
 /* Steps exposed one at a time for the tests. */
 int32_t orc_requant(int64_t x, int32_t b, int32_t c);

@@ -61,6 +61,16 @@ def _load():
         lib.orc_linear.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
                                    C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int64]
         lib.orc_linear.restype = C.c_int
+        lib.orc_shiftgelu.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                                      C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                      C.c_int64, C.c_int64, C.c_void_p]
+        lib.orc_shiftgelu.restype = C.c_int
+        lib.orc_isqrt10.argtypes = [C.c_int64]
+        lib.orc_isqrt10.restype = C.c_int64
+        lib.orc_ilayernorm.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                                       C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                       C.c_int64, C.c_int64, C.c_void_p]
+        lib.orc_ilayernorm.restype = C.c_int
         lib.orc_requant.restype = C.c_int32
         lib.orc_requant_array.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
                                           C.c_void_p]
@@ -191,3 +201,45 @@ def linear(x: np.ndarray, w: np.ndarray, b: int, c: int, rows=None) -> np.ndarra
     if rc != 0:
         raise ValueError(f"orc_linear: invalid arguments ({rc})")
     return out[r0:r1]
+
+
+def shiftgelu(x: np.ndarray, params: Dict[str, int], rows=None, dump=False):
+    """ShiftGELU of x [rows, cols] int8 -> int8 (and, with dump, an int64 array
+    [rows, cols, 4] of (Ip, e1, e2, sigmoid code) per element)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    M, N = x.shape
+    r0, r1 = (0, M) if rows is None else rows
+    out = np.zeros((M, N), np.int8)
+    sig = np.zeros((M, N, 4), np.int64) if dump else None
+    rc = lib.orc_shiftgelu(x.ctypes.data, M, N, params["i0"], params["exp_frac_bits"],
+                           params["intdiv_m"], params["k_out"], params["b"], params["c"],
+                           out.ctypes.data, r0, r1, sig.ctypes.data if dump else None)
+    if rc != 0:
+        raise ValueError(f"orc_shiftgelu: invalid arguments ({rc})")
+    return (out[r0:r1], sig[r0:r1]) if dump else out[r0:r1]
+
+
+def isqrt10(v: int) -> int:
+    return int(_load().orc_isqrt10(int(v)))
+
+
+def ilayernorm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, params: Dict[str, int],
+               rows=None, dump=False):
+    """I-LayerNorm of x [rows, cols] int8 with gamma int8 [cols], beta int32
+    [cols] -> int8 (and per-row mean, var, sd, floor(2^M / sd))."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    g = np.ascontiguousarray(gamma, dtype=np.int8)
+    be = np.ascontiguousarray(beta, dtype=np.int32)
+    M, N = x.shape
+    r0, r1 = (0, M) if rows is None else rows
+    out = np.zeros((M, N), np.int8)
+    st = np.zeros((M, 4), np.int64) if dump else None
+    rc = lib.orc_ilayernorm(x.ctypes.data, g.ctypes.data, be.ctypes.data, M, N,
+                            params["norm_frac_bits"], params["intdiv_m"], params["b"],
+                            params["c"], out.ctypes.data, r0, r1,
+                            st.ctypes.data if dump else None)
+    if rc != 0:
+        raise ValueError(f"orc_ilayernorm: invalid arguments ({rc})")
+    return (out[r0:r1], st[r0:r1]) if dump else out[r0:r1]

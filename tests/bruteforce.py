@@ -66,3 +66,40 @@ def attention(q, k, v, p):
                     o = sum(wts[j] * int(v[b][h][j][t]) for j in range(N))
                     out[b][h][i][t] = requant(o, p["pv_b"], p["pv_c"])
     return out
+
+
+def shiftgelu_row(xs, p):
+    """ShiftGELU (I-ViT sec. 3.4) of one row of ints."""
+    ip = [x + fl(x, 2) + fl(x, 8) + fl(x, 16) for x in xs]
+    imax = max([0] + ip)
+    e2 = shift_exp(-imax, p["i0"], p["exp_frac_bits"])
+    m, k = p["intdiv_m"], p["k_out"]
+    out = []
+    for x, v in zip(xs, ip):
+        e1 = shift_exp(v - imax, p["i0"], p["exp_frac_bits"])
+        sig = 0
+        if e1:
+            sig = min(fl(fl(2 ** m, e1 + e2) * e1, 2 ** (m - k + 1)), 2 ** (k - 1) - 1)
+        out.append(requant(x * sig, p["b"], p["c"]))
+    return out
+
+
+def newton_isqrt10(v):
+    if v <= 0:
+        return 0
+    r = 2 ** (v.bit_length() // 2)
+    for _ in range(10):
+        r = fl(r + fl(v, r), 2)
+    return r
+
+
+def ilayernorm_row(xs, gamma, beta, p):
+    """I-LayerNorm (I-ViT sec. 3.5) of one row of ints."""
+    n = len(xs)
+    mean = fl(sum(xs), n)
+    var = fl(sum((x - mean) ** 2 for x in xs), n)
+    sd = newton_isqrt10(var) or 1
+    m, f = p["intdiv_m"], p["norm_frac_bits"]
+    fs = fl(2 ** m, sd)
+    return [requant(fl((x - mean) * fs, 2 ** (m - f)) * int(g) + int(bt), p["b"], p["c"])
+            for x, g, bt in zip(xs, gamma, beta)]
