@@ -34,7 +34,9 @@ IQLINEAR_PLAIN = 0
 IQLINEAR_QKV_HEADS = 1
 
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
-            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy")
+            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy",
+            "iqgelu_create", "iqgelu_forward", "iqgelu_destroy",
+            "iqlayernorm_create", "iqlayernorm_forward", "iqlayernorm_destroy")
 
 
 class iqattn_params(C.Structure):
@@ -48,6 +50,16 @@ class iqlinear_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "rows", "in_features", "out_features", "layout", "batch", "seq_len", "heads",
         "head_dim")] + [("b", C.c_int32 * 3), ("c", C.c_int32 * 3)]
+
+
+class iqgelu_params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "rows", "cols", "i0", "exp_frac_bits", "intdiv_m", "k_out", "b", "c")]
+
+
+class iqlayernorm_params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "rows", "cols", "norm_frac_bits", "intdiv_m", "b", "c")]
 
 
 class IQAttnError(RuntimeError):
@@ -81,6 +93,18 @@ def load_library():
         lib.iqlinear_forward.restype = C.c_int
         lib.iqlinear_destroy.argtypes = [C.c_void_p]
         lib.iqlinear_destroy.restype = C.c_int
+        lib.iqgelu_create.argtypes = [C.POINTER(iqgelu_params), C.POINTER(C.c_void_p)]
+        lib.iqgelu_create.restype = C.c_int
+        lib.iqgelu_forward.argtypes = [C.c_void_p] * 4
+        lib.iqgelu_forward.restype = C.c_int
+        lib.iqgelu_destroy.argtypes = [C.c_void_p]
+        lib.iqgelu_destroy.restype = C.c_int
+        lib.iqlayernorm_create.argtypes = [C.POINTER(iqlayernorm_params), C.POINTER(C.c_void_p)]
+        lib.iqlayernorm_create.restype = C.c_int
+        lib.iqlayernorm_forward.argtypes = [C.c_void_p] * 6
+        lib.iqlayernorm_forward.restype = C.c_int
+        lib.iqlayernorm_destroy.argtypes = [C.c_void_p]
+        lib.iqlayernorm_destroy.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -250,3 +274,133 @@ class IQLinear:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------- ShiftGELU / I-LayerNorm
+def _fill(struct_cls, fields, params: Dict[str, object]):
+    p = struct_cls()
+    for name in fields:
+        setattr(p, name, int(params[name]))
+    return p
+
+
+def make_gelu_params(params: Dict[str, object]) -> iqgelu_params:
+    return _fill(iqgelu_params, ("rows", "cols", "i0", "exp_frac_bits", "intdiv_m", "k_out",
+                                 "b", "c"), params)
+
+
+def make_layernorm_params(params: Dict[str, object]) -> iqlayernorm_params:
+    return _fill(iqlayernorm_params, ("rows", "cols", "norm_frac_bits", "intdiv_m", "b", "c"),
+                 params)
+
+
+def _create(fn, p, where) -> int:
+    ctx = C.c_void_p()
+    rc = fn(C.byref(p), C.byref(ctx))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, where)
+    return ctx.value
+
+
+def iqgelu_create(p: iqgelu_params) -> int:
+    return _create(load_library().iqgelu_create, p, "iqgelu_create")
+
+
+def iqgelu_forward(ctx: int, x, out, stream=None) -> None:
+    ptr = lambda t: None if t is None else C.c_void_p(t.data_ptr())  # noqa: E731
+    rc = load_library().iqgelu_forward(C.c_void_p(ctx), ptr(x), ptr(out),
+                                       C.c_void_p(_stream_handle(stream)))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqgelu_forward")
+
+
+def iqgelu_destroy(ctx: Optional[int]) -> None:
+    rc = load_library().iqgelu_destroy(C.c_void_p(ctx) if ctx else None)
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqgelu_destroy")
+
+
+def iqlayernorm_create(p: iqlayernorm_params) -> int:
+    return _create(load_library().iqlayernorm_create, p, "iqlayernorm_create")
+
+
+def iqlayernorm_forward(ctx: int, x, gamma, beta, out, stream=None) -> None:
+    ptr = lambda t: None if t is None else C.c_void_p(t.data_ptr())  # noqa: E731
+    rc = load_library().iqlayernorm_forward(C.c_void_p(ctx), ptr(x), ptr(gamma), ptr(beta),
+                                            ptr(out), C.c_void_p(_stream_handle(stream)))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlayernorm_forward")
+
+
+def iqlayernorm_destroy(ctx: Optional[int]) -> None:
+    rc = load_library().iqlayernorm_destroy(C.c_void_p(ctx) if ctx else None)
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlayernorm_destroy")
+
+
+def _check(name, t, dtype, shape):
+    import torch
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {shape}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    del torch
+
+
+class _Owner:
+    _destroy = None
+
+    def close(self):
+        if self.ctx:
+            type(self)._destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class IQGelu(_Owner):
+    """Owns one ShiftGELU context: x [rows, cols] int8 -> int8."""
+    _destroy = staticmethod(iqgelu_destroy)
+
+    def __init__(self, params: Dict[str, object]):
+        self.params = dict(params)
+        self.ctx = iqgelu_create(make_gelu_params(self.params))
+
+    def forward(self, x, out=None, stream=None):
+        import torch
+        shape = (self.params["rows"], self.params["cols"])
+        _check("x", x, torch.int8, shape)
+        out = out if out is not None else torch.empty(shape, dtype=torch.int8, device=x.device)
+        _check("out", out, torch.int8, shape)
+        iqgelu_forward(self.ctx, x, out, stream)
+        return out
+
+    __call__ = forward
+
+
+class IQLayerNorm(_Owner):
+    """Owns one I-LayerNorm context: x [rows, cols] int8, gamma [cols] int8,
+    beta [cols] int32 -> int8."""
+    _destroy = staticmethod(iqlayernorm_destroy)
+
+    def __init__(self, params: Dict[str, object]):
+        self.params = dict(params)
+        self.ctx = iqlayernorm_create(make_layernorm_params(self.params))
+
+    def forward(self, x, gamma, beta, out=None, stream=None):
+        import torch
+        rows, cols = self.params["rows"], self.params["cols"]
+        _check("x", x, torch.int8, (rows, cols))
+        _check("gamma", gamma, torch.int8, (cols,))
+        _check("beta", beta, torch.int32, (cols,))
+        out = out if out is not None else torch.empty((rows, cols), dtype=torch.int8,
+                                                      device=x.device)
+        _check("out", out, torch.int8, (rows, cols))
+        iqlayernorm_forward(self.ctx, x, gamma, beta, out, stream)
+        return out
+
+    __call__ = forward

@@ -277,10 +277,10 @@ class LayerNormWorkload:
 
 
 def layernorm_params(seed: int) -> Dict[str, int]:
-    """7 fraction bits on the normalised value, M = 23 for floor(2^M / sd);
+    """7 fraction bits on the normalised value, M = 22 for floor(2^M / sd);
     output pair b uniform in [2^14, 2^15), c = 22."""
     b = Stream(seed, S_LNPARAMS).randint(1 << 14, (1 << 15) - 1, 1)
-    return dict(norm_frac_bits=7, intdiv_m=23, b=int(b[0]), c=22)
+    return dict(norm_frac_bits=7, intdiv_m=22, b=int(b[0]), c=22)
 
 
 def make_layernorm(rows: int, cols: int, seed: int, name: str = "custom",

@@ -19,7 +19,7 @@ def _declared_functions():
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(iq(?:attn|linear)_\w+)\s*\(", text))
+            names |= set(re.findall(r"\b(iq(?:attn|linear|gelu|layernorm)_\w+)\s*\(", text))
     return names
 
 
@@ -139,3 +139,57 @@ def test_linear_null_arguments(lib):
     assert lib.iqlinear_create(None, None) == IQ.IQATTN_E_NULL
     assert lib.iqlinear_destroy(None) == IQ.IQATTN_OK
     assert lib.iqlinear_forward(None, None, None, None, None, None, None) == IQ.IQATTN_E_NULL
+
+
+def _gelu_rc(lib, **over):
+    p = dict(rows=4, cols=64, i0=16, exp_frac_bits=22, intdiv_m=40, k_out=8, b=20000, c=22)
+    p.update(over)
+    ctx = C.c_void_p(12345)
+    rc = lib.iqgelu_create(C.byref(IQ.make_gelu_params(p)), C.byref(ctx))
+    return rc, ctx.value
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(rows=-1), IQ.IQATTN_E_SHAPE), (dict(cols=0), IQ.IQATTN_E_SHAPE),
+    (dict(cols=8), IQ.IQATTN_E_SHAPE), (dict(cols=72), IQ.IQATTN_E_SHAPE),
+    (dict(cols=16400), IQ.IQATTN_E_SHAPE), (dict(rows=1 << 20, cols=4096), IQ.IQATTN_E_SHAPE),
+    (dict(i0=0), IQ.IQATTN_E_INVAL), (dict(i0=32769), IQ.IQATTN_E_INVAL),
+    (dict(exp_frac_bits=31), IQ.IQATTN_E_INVAL), (dict(k_out=1), IQ.IQATTN_E_INVAL),
+    (dict(k_out=9), IQ.IQATTN_E_INVAL), (dict(intdiv_m=6), IQ.IQATTN_E_INVAL),
+    (dict(intdiv_m=41), IQ.IQATTN_E_INVAL), (dict(b=0), IQ.IQATTN_E_INVAL),
+    (dict(c=63), IQ.IQATTN_E_INVAL), (dict(c=-1), IQ.IQATTN_E_INVAL),
+])
+def test_gelu_create_rejects_bad_parameters_before_any_device_call(lib, over, code):
+    rc, ctx = _gelu_rc(lib, **over)
+    assert rc == code
+    assert ctx is None
+
+
+def _ln_rc(lib, **over):
+    p = dict(rows=4, cols=64, norm_frac_bits=7, intdiv_m=22, b=20000, c=22)
+    p.update(over)
+    ctx = C.c_void_p(12345)
+    rc = lib.iqlayernorm_create(C.byref(IQ.make_layernorm_params(p)), C.byref(ctx))
+    return rc, ctx.value
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(rows=-1), IQ.IQATTN_E_SHAPE), (dict(cols=0), IQ.IQATTN_E_SHAPE),
+    (dict(cols=40), IQ.IQATTN_E_SHAPE), (dict(cols=16384 + 16), IQ.IQATTN_E_SHAPE),
+    (dict(norm_frac_bits=-1), IQ.IQATTN_E_INVAL), (dict(norm_frac_bits=9), IQ.IQATTN_E_INVAL),
+    (dict(intdiv_m=6), IQ.IQATTN_E_INVAL), (dict(intdiv_m=23), IQ.IQATTN_E_INVAL),
+    (dict(b=0), IQ.IQATTN_E_INVAL), (dict(c=63), IQ.IQATTN_E_INVAL),
+])
+def test_layernorm_create_rejects_bad_parameters_before_any_device_call(lib, over, code):
+    rc, ctx = _ln_rc(lib, **over)
+    assert rc == code
+    assert ctx is None
+
+
+def test_block_null_arguments(lib):
+    assert lib.iqgelu_create(None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqgelu_destroy(None) == IQ.IQATTN_OK
+    assert lib.iqgelu_forward(None, None, None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqlayernorm_create(None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqlayernorm_destroy(None) == IQ.IQATTN_OK
+    assert lib.iqlayernorm_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL

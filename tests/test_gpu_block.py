@@ -1,0 +1,202 @@
+"""Bit-exact parity of ShiftGELU and I-LayerNorm (through the C-ABI) with the
+CPU oracle: every kernel shape (16 and 64 lanes a row, 1..16 chunks a lane,
+affine parameters in registers and in LDS), ragged row and column counts,
+every (row maximum, x) pair of the ShiftGELU table, constant and extreme rows,
+both requantisation paths, and the ViT-B shapes at full size."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from integer_only_quantized_int8_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "no GPU visible"
+    return torch
+
+
+def gelu_gpu(torch, x, params):
+    """Run ShiftGELU on x [rows, cols]; the row after the output must stay untouched."""
+    from integer_only_quantized_int8_amd.iqattn import IQGelu
+    rows, cols = x.shape
+    P = dict(params, rows=rows, cols=cols)
+    op = IQGelu(P)
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    buf = torch.full((rows + 1, cols), 99, dtype=torch.int8, device=dev)
+    op.forward(xd, buf[:rows])
+    torch.cuda.synchronize()
+    res = buf.cpu().numpy()
+    op.close()
+    assert np.all(res[rows] == 99), "write past the output"
+    return res[:rows]
+
+
+def ln_gpu(torch, x, gamma, beta, params):
+    from integer_only_quantized_int8_amd.iqattn import IQLayerNorm
+    rows, cols = x.shape
+    P = dict(params, rows=rows, cols=cols)
+    op = IQLayerNorm(P)
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    gd = torch.from_numpy(np.ascontiguousarray(gamma, dtype=np.int8)).to(dev)
+    bd = torch.from_numpy(np.ascontiguousarray(beta, dtype=np.int32)).to(dev)
+    buf = torch.full((rows + 1, cols), 99, dtype=torch.int8, device=dev)
+    op.forward(xd, gd, bd, buf[:rows])
+    torch.cuda.synchronize()
+    res = buf.cpu().numpy()
+    op.close()
+    assert np.all(res[rows] == 99), "write past the output"
+    return res[:rows]
+
+
+def _mismatch(got, want):
+    bad = np.argwhere(got != want)
+    if len(bad):
+        r, c = bad[0]
+        return f"{len(bad)} mismatches, first at ({r}, {c}): got {got[r, c]} want {want[r, c]}"
+    return ""
+
+
+# ---------------------------------------------------------------- ShiftGELU
+GELU_SHAPES = [(1, 16), (3, 48), (17, 256), (33, 272), (5, 768), (64, 1024), (9, 2048),
+               (7, 2064), (3, 3072), (2, 4096), (3, 5120), (2, 8208), (2, 16384), (1000, 64)]
+
+
+@pytest.mark.parametrize("rows,cols", GELU_SHAPES)
+def test_gelu_shapes(torch_dev, rows, cols):
+    _say(f"gelu shape {rows}x{cols}")
+    wl = W.make_gelu(rows, cols, seed=rows * 7 + cols)
+    got = gelu_gpu(torch_dev, wl.x, wl.params)
+    want = oracle.shiftgelu(wl.x, wl.params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+@pytest.mark.parametrize("params", [
+    dict(i0=16, exp_frac_bits=22, intdiv_m=40, k_out=8, b=20000, c=22),
+    dict(i0=16, exp_frac_bits=8, intdiv_m=30, k_out=8, b=1 << 14, c=21),
+    dict(i0=7, exp_frac_bits=12, intdiv_m=36, k_out=6, b=99, c=9),
+    dict(i0=1, exp_frac_bits=0, intdiv_m=20, k_out=2, b=1, c=0),
+    dict(i0=32768, exp_frac_bits=30, intdiv_m=40, k_out=8, b=(1 << 31) - 1, c=62),
+    dict(i0=3, exp_frac_bits=30, intdiv_m=7, k_out=8, b=(1 << 31) - 1, c=40),
+])
+def test_gelu_every_table_entry(torch_dev, params):
+    """Rows min(x, m) over all 256 int8 values for m = -1 .. 127 use every
+    (clamped row maximum, x) pair the operator can meet."""
+    _say(f"gelu table {params}")
+    full = np.arange(-128, 128, dtype=np.int64)
+    x = np.array([np.minimum(full, m) for m in range(-1, 128)], dtype=np.int8)
+    got = gelu_gpu(torch_dev, x, params)
+    want = oracle.shiftgelu(x, params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+def test_gelu_constant_and_extreme_rows(torch_dev):
+    _say("gelu constant rows")
+    vals = [-128, -127, -1, 0, 1, 127]
+    x = np.array([[v] * 96 for v in vals] + [[-128, 127] * 48, [127, -128] * 48], np.int8)
+    P = W.gelu_params(1)
+    got = gelu_gpu(torch_dev, x, P)
+    assert not _mismatch(got, oracle.shiftgelu(x, P))
+
+
+def test_gelu_vitb_full_size(torch_dev):
+    """The MLP activation of ViT-B at batch 128 (25216 x 3072) in the launch
+    configuration the benchmark times, every element against the oracle."""
+    wl = W.gelu_workload("vitb_mlp_b128_n197_c3072")
+    _say(f"gelu vitb {wl.x.shape}")
+    got = gelu_gpu(torch_dev, wl.x, wl.params)
+    want = oracle.shiftgelu(wl.x, wl.params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+# ---------------------------------------------------------------- I-LayerNorm
+LN_SHAPES = [(1, 16), (3, 48), (17, 256), (33, 272), (5, 768), (64, 1024), (9, 1280),
+             (9, 2048), (7, 2064), (3, 3072), (2, 5120), (2, 16384), (1000, 64)]
+FAST = dict(norm_frac_bits=7, intdiv_m=22, b=20000, c=22)
+SLOW = dict(norm_frac_bits=8, intdiv_m=22, b=(1 << 31) - 1, c=45)
+
+
+@pytest.mark.parametrize("rows,cols", LN_SHAPES)
+@pytest.mark.parametrize("params", [FAST, SLOW], ids=["fast", "slow"])
+def test_layernorm_shapes(torch_dev, rows, cols, params):
+    _say(f"layernorm shape {rows}x{cols} {params}")
+    wl = W.make_layernorm(rows, cols, seed=rows * 13 + cols)
+    got = ln_gpu(torch_dev, wl.x, wl.gamma, wl.beta, params)
+    want = oracle.ilayernorm(wl.x, wl.gamma, wl.beta, params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+@pytest.mark.parametrize("params", [
+    FAST, SLOW, dict(norm_frac_bits=0, intdiv_m=0, b=1, c=0),
+    dict(norm_frac_bits=8, intdiv_m=8, b=1, c=1), dict(norm_frac_bits=4, intdiv_m=22, b=3, c=32),
+    dict(norm_frac_bits=7, intdiv_m=20, b=(1 << 30), c=32),
+    dict(norm_frac_bits=7, intdiv_m=22, b=1, c=31),
+])
+def test_layernorm_extreme_rows(torch_dev, params):
+    """Constant rows (var 0), rows of +-a, rows at the int8 limits, one
+    outlier per row, every variance from 0 to its maximum; gamma at -128 and
+    127, beta at the int32 limits (the saturating add of the fast path)."""
+    _say(f"layernorm extremes {params}")
+    cols = 272
+    rng = np.random.default_rng(5)
+    rows = []
+    for v in (-128, -1, 0, 5, 127):
+        rows.append(np.full(cols, v))
+    for a in (1, 2, 3, 16, 64, 127):
+        rows.append(np.array([a, -a] * (cols // 2)))
+    rows.append(np.array([-128, 127] * (cols // 2)))
+    for sd in range(0, 128, 3):   # spread from 0 to 127
+        rows.append(np.clip(np.round(rng.standard_normal(cols) * sd), -128, 127))
+    out1 = np.zeros(cols)
+    out1[17] = 127
+    rows.append(out1)
+    x = np.array(rows, dtype=np.int8)
+    gamma = rng.integers(-128, 128, cols).astype(np.int8)
+    gamma[:4] = [-128, 127, 0, 1]
+    beta = rng.integers(-(1 << 31), 1 << 31, cols, dtype=np.int64).astype(np.int32)
+    beta[:6] = [-(1 << 31), (1 << 31) - 1, 0, -1, 1 << 30, -(1 << 30)]
+    got = ln_gpu(torch_dev, x, gamma, beta, params)
+    want = oracle.ilayernorm(x, gamma, beta, params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+def test_layernorm_vitb_full_size(torch_dev):
+    """The LayerNorm input of ViT-B at batch 128 (25216 x 768) in the launch
+    configuration the benchmark times, every element against the oracle."""
+    wl = W.layernorm_workload("vitb_ln_b128_n197_c768")
+    _say(f"layernorm vitb {wl.x.shape}")
+    got = ln_gpu(torch_dev, wl.x, wl.gamma, wl.beta, wl.params)
+    want = oracle.ilayernorm(wl.x, wl.gamma, wl.beta, wl.params)
+    assert not _mismatch(got, want), _mismatch(got, want)
+
+
+def test_block_zero_rows_and_errors(torch_dev):
+    """rows = 0 is a no-op; bad pointers are rejected before any launch."""
+    import ctypes as C
+    from integer_only_quantized_int8_amd import iqattn as IQ
+    g = IQ.IQGelu(dict(W.gelu_params(1), rows=0, cols=64))
+    IQ.iqgelu_forward(g.ctx, None, None)
+    g.close()
+    ln = IQ.IQLayerNorm(dict(W.layernorm_params(1), rows=0, cols=64))
+    IQ.iqlayernorm_forward(ln.ctx, None, None, None, None)
+    ln.close()
+    g = IQ.IQGelu(dict(W.gelu_params(1), rows=2, cols=64))
+    x = torch_dev.zeros((2, 80), dtype=torch_dev.int8, device="cuda:0")
+    lib = IQ.load_library()
+    assert lib.iqgelu_forward(C.c_void_p(g.ctx), C.c_void_p(x.data_ptr() + 1),
+                              C.c_void_p(x.data_ptr() + 16), None) == IQ.IQATTN_E_ALIGN
+    assert lib.iqgelu_forward(C.c_void_p(g.ctx), None, C.c_void_p(x.data_ptr()),
+                              None) == IQ.IQATTN_E_NULL
+    g.close()
