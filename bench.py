@@ -149,6 +149,78 @@ def bench_linear(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_block(args):
+    """Time ShiftGELU or I-LayerNorm on the ViT-B shapes (MLP activation
+    25216 x 3072, LayerNorm input 25216 x 768); roofline against HBM."""
+    import numpy as np
+    import torch
+    from integer_only_quantized_int8_amd import workloads as W
+    from integer_only_quantized_int8_amd.iqattn import IQGelu, IQLayerNorm
+    dev = torch.device("cuda:0")
+    if args.block == "gelu":
+        wl = W.gelu_workload("vitb_mlp_b128_n197_c3072")
+        op = IQGelu(dict(wl.params, rows=wl.rows, cols=wl.cols))
+        x = torch.from_numpy(wl.x).to(dev)
+        out = torch.empty_like(x)
+        run = lambda: op.forward(x, out)  # noqa: E731
+        affine_bytes = 0
+    else:
+        wl = W.layernorm_workload("vitb_ln_b128_n197_c768")
+        op = IQLayerNorm(dict(wl.params, rows=wl.rows, cols=wl.cols))
+        x = torch.from_numpy(wl.x).to(dev)
+        g = torch.from_numpy(wl.gamma).to(dev)
+        b = torch.from_numpy(wl.beta).to(dev)
+        out = torch.empty_like(x)
+        run = lambda: op.forward(x, g, b, out)  # noqa: E731
+        affine_bytes = 5 * wl.cols
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            run()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = g0.elapsed_time(g1) / args.steps
+    elems = wl.rows * wl.cols
+    algo = float(2 * elems + affine_bytes)  # int8 in + int8 out (+ gamma, beta)
+    gbs = algo / (kern_ms * 1e-3) / 1e9
+    res = {"metric": f"integer-only {'ShiftGELU' if args.block == 'gelu' else 'I-LayerNorm'} "
+                     f"Gelem/s, {wl.name}",
+           "value": round(elems / (step_ms * 1e-3) / 1e9, 2), "unit": "Gelem/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+           "data": "synthetic (seeded int8 activations)",
+           "config": {"workload": wl.name, "rows": wl.rows, "cols": wl.cols},
+           "kernel_us_mean": round(kern_ms * 1e3, 3),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": int(algo)}}
+    if not args.no_cpu:
+        import oracle
+        t1 = time.perf_counter()
+        if args.block == "gelu":
+            oracle.shiftgelu(wl.x, wl.params)
+        else:
+            oracle.ilayernorm(wl.x, wl.gamma, wl.beta, wl.params)
+        cpu_s = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": round(elems / cpu_s / 1e9, 4), "unit": "Gelem/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the whole {wl.rows} x {wl.cols} tensor, "
+                                         f"{cpu_s:.2f} s single-threaded C -O2 on {cpu_model()}"}
+    op.close()
+    print(json.dumps(res), flush=True)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -173,6 +245,8 @@ def main():
     ap.add_argument("--linear", default=None,
                     help="time an int8 linear layer instead (workload name from "
                          "workloads.LINEAR_CONFIGS, e.g. vitb_qkv_b128_n197_c768)")
+    ap.add_argument("--block", default=None, choices=("gelu", "layernorm"),
+                    help="time ShiftGELU or I-LayerNorm on the ViT-B shapes instead")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter files and exit (no GPU use)")
@@ -202,6 +276,9 @@ def main():
 
     if args.linear:
         bench_linear(args)
+        return
+    if args.block:
+        bench_block(args)
         return
 
     t0 = time.time()

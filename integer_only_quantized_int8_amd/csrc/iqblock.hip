@@ -57,7 +57,9 @@ struct LnDev {
   int8_t* out;
   int32_t rows, cols;
   int32_t m, f;        // IntDiv exponent M, fraction bits F
-  int32_t b, c, bm;    // dyadic pair; bm = b << (32 - c) (fast requantisation)
+  int32_t b, c;        // dyadic pair
+  int32_t bm, ywin;    // b << (32 - c) (RQ_MULHI); ceil(127 * 2^c / b) (RQ_WIN)
+  uint32_t sqmask[6];  // bit k: ten Newton steps on k^2 - 1 end on k (not k - 1)
 };
 
 // ---------------------------------------------------------------- ShiftGELU
@@ -186,6 +188,8 @@ __device__ __forceinline__ int32_t udiv_small(int32_t a, int32_t b) {
   return q;
 }
 
+// The ten Newton steps I <- (I + floor(v / I)) >> 1 from I = 2^floor(bits(v)/2)
+// for 0 <= v < 2^15.
 __device__ __forceinline__ int32_t isqrt_newton10(int32_t v) {
   if (v <= 0) return 0;
   const int bits = 32 - __builtin_clz((uint32_t)v);
@@ -195,13 +199,78 @@ __device__ __forceinline__ int32_t isqrt_newton10(int32_t v) {
   return r;
 }
 
-// gamma and beta of a lane's chunks stay in registers (16 + 64 bytes a chunk)
-// up to 4 chunks; with more they are read per row from a copy in LDS.
-constexpr bool ln_affine_in_regs(int nch) { return nch <= 4; }
+// For v < 2^15 the ten steps end on floor(sqrt v), except at v = k^2 - 1, where
+// the integer iteration alternates between k - 1 and k and the tenth step may
+// hold either; flags[k] records which (k < 192), so that the streaming kernel
+// can take the exact square root and one mask bit instead of ten divisions.
+__global__ void iqln_newton_flags(uint8_t* flags) {
+  const int k = threadIdx.x;
+  if (k >= 192) return;
+  const int32_t v = k * k - 1;
+  flags[k] = (v >= 1 && v < (1 << 15) && isqrt_newton10(v) == k) ? 1 : 0;
+}
 
-template <int G, int NCH, bool FAST>
+// The ten-step result for 1 <= v < 2^15: floor(sqrt v) by the float square
+// root with an exact integer correction, raised to k where v = k^2 - 1 and
+// the mask bit k is set.
+__device__ __forceinline__ int32_t isqrt_newton10_fast(int32_t v, const uint32_t* mask) {
+  int32_t s = (int32_t)__builtin_sqrtf((float)v);
+  if (s * s > v) --s;
+  if ((s + 1) * (s + 1) <= v) ++s;
+  const int32_t k = s + 1;
+  if (k * k - 1 == v) {
+    const uint64_t lo = ((uint64_t)mask[1] << 32) | mask[0];
+    const uint64_t mid = ((uint64_t)mask[3] << 32) | mask[2];
+    const uint64_t hi = ((uint64_t)mask[5] << 32) | mask[4];
+    const uint64_t m = k < 64 ? lo : (k < 128 ? mid : hi);
+    if ((m >> (k & 63)) & 1) s = k;
+  }
+  return s;
+}
+
+// floor(a / b) for b >= 1 and |a / b| < 2^22 with rb ~ 1/b from v_rcp_f32:
+// the float estimate is within 1 of the quotient (relative error below
+// 2^-22), and up to two exact integer correction steps each way make it exact.
+__device__ __forceinline__ int32_t floordiv_est(int32_t a, int32_t b, float rb) {
+  int32_t q = (int32_t)floorf((float)a * rb);
+  int32_t r = a - q * b;
+  if (r < 0) { --q; r += b; if (r < 0) { --q; r += b; } }
+  if (r >= b) { ++q; r -= b; if (r >= b) ++q; }
+  return q;
+}
+
+// sat32(a * b + c) for a, b in the signed 24-bit range: v_mad_i32_i24 with the
+// clamp bit, which saturates the integer result.
+__device__ __forceinline__ int32_t mad24_sat(int32_t a, int32_t b, int32_t c) {
+  int32_t r;
+  asm("v_mad_i32_i24 %0, %1, %2, %3 clamp" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// median of (x, lo, hi) = clamp of x to [lo, hi] for lo <= hi (one v_med3_i32;
+// the compiler emits a min and a max when it cannot see lo <= hi).
+__device__ __forceinline__ int32_t med3_i32(int32_t x, int32_t lo, int32_t hi) {
+  int32_t r;
+  asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(lo), "s"(hi));
+  return r;
+}
+
+// Requantisation of y = nrm * gamma + beta, exact in all three forms:
+//   RQ_WIDE: 64-bit (b * y) >> c;
+//   RQ_MULHI: int32 y saturated, mulhi(y, b << (32 - c)) (when b << (32 - c) <
+//     2^31 and a saturated y clips either way);
+//   RQ_WIN: y saturated, then clamped to +-ywin = ceil(127 * 2^c / b) (beyond
+//     it the clipped result is +-127 already), then a 24-bit multiply by b and a
+//     shift (when b, ywin < 2^23 and 127 * 2^c + b < 2^31 keep it exact).
+constexpr int RQ_WIDE = 0, RQ_MULHI = 1, RQ_WIN = 2;
+
+// gamma and beta sit in LDS, one copy per block, laid out chunk-major: entry
+// ((k * 4 + j) * G + lane) holds the 4 columns 16 * (lane + G * k) + 4 j ..,
+// so that the 16-byte reads of consecutive lanes hit consecutive banks
+// (column-major order would put every fourth lane on the same banks).  This
+// measured faster than keeping them in registers, which costs waves.
+template <int G, int NCH, int RQ>
 __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
-  constexpr bool REGS = ln_affine_in_regs(NCH);
   constexpr int RPW = 64 / G;
   constexpr int RPB = RPW * (kLnThreads / 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -212,36 +281,48 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
   const __amdgpu_buffer_rsrc_t gr = buf_rsrc(p.gamma, (uint32_t)p.cols);
   const __amdgpu_buffer_rsrc_t br = buf_rsrc(p.beta, (uint32_t)p.cols * 4u);
 
-  // LDS copy (REGS false): beta [cols] int32, then gamma [cols] int8
-  extern __shared__ __attribute__((aligned(16))) int32_t ln_aff[];
-  v4i gam[REGS ? NCH : 1], bet[REGS ? NCH : 1][4];
-  if constexpr (REGS) {
+  // this lane's chunks of the group of rows starting at r0 (zeros past the row
+  // end; a row past the last reads the last row and is not stored)
+  auto load_rows = [&](int r0, v4i* d) {
+    const int row = r0 + wave * RPW + sub;
+    const int rowc = row < p.rows ? row : p.rows - 1;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int col = 16 * (gl + G * k);
-      gam[k] = buf_load<v4i>(gr, col);  // past the end: zeros
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bet[k][j] = buf_load<v4i>(br, 4 * col + 16 * j);
+      d[k] = buf_load<v4i>(xr, rowc * p.cols + (col < p.cols ? col : 0));
     }
-  } else {
-    for (int i = threadIdx.x; i < p.cols / 4; i += kLnThreads)
-      reinterpret_cast<v4i*>(ln_aff)[i] = buf_load<v4i>(br, 16 * i);
-    for (int i = threadIdx.x; i < p.cols / 16; i += kLnThreads)
-      reinterpret_cast<v4i*>(ln_aff + p.cols)[i] = buf_load<v4i>(gr, 16 * i);
-    __syncthreads();
-  }
+  };
+  const int step = gridDim.x * RPB;
+  int r0 = blockIdx.x * RPB;
+  v4i d[NCH];
+  load_rows(r0, d);  // in flight while gamma and beta are staged
 
-  for (int r0 = blockIdx.x * RPB; r0 < p.rows; r0 += gridDim.x * RPB) {
+  // LDS copy: beta entries, then gamma widened to int32, NENT of each
+  extern __shared__ __attribute__((aligned(16))) int32_t ln_aff[];
+  constexpr int NENT = 4 * G * NCH;  // 16-byte entries per table
+  for (int i = threadIdx.x; i < NENT; i += kLnThreads) {
+    const int gi = i % G, kj = i / G;
+    const int col = 16 * (gi + G * (kj >> 2)) + 4 * (kj & 3);  // past cols: zeros
+    reinterpret_cast<v4i*>(ln_aff)[i] = buf_load<v4i>(br, 4 * col);
+    const int32_t g4 = __builtin_amdgcn_raw_buffer_load_b32(gr, col, 0, 0);
+    v4i g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) g[t] = (int8_t)(g4 >> (8 * t));
+    reinterpret_cast<v4i*>(ln_aff)[NENT + i] = g;
+  }
+  __syncthreads();
+  const float rcols = __builtin_amdgcn_rcpf((float)p.cols);
+  const int32_t sh = p.m - p.f;
+  const int32_t nywin = -p.ywin;
+
+  for (; r0 < p.rows; r0 += step) {
     const int row = r0 + wave * RPW + sub;
     const bool rv = row < p.rows;
-    const int rowc = rv ? row : p.rows - 1;
-    v4i d[NCH];
     int32_t s1 = 0, s2 = 0;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int col = 16 * (gl + G * k);
       const bool cv = col < p.cols;
-      d[k] = buf_load<v4i>(xr, rowc * p.cols + (cv ? col : 0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         d[k][j] = cv ? d[k][j] : 0;
@@ -251,45 +332,40 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
     }
     s1 = group_sum_i32<G>(s1);   // |s1| <= 128 * 16384 = 2^21
     s2 = group_sum_i32<G>(s2);   // s2 <= 2^14 * 2^14 = 2^28
-    // floor divisions by cols in double: the correctly rounded quotient of
-    // integers below 2^31 by a divisor below 2^15 never reaches the next integer
-    const int32_t mean = (int32_t)floor((double)s1 / (double)p.cols);
-    const int32_t cen = s2 - 2 * mean * s1 + p.cols * mean * mean;  // sum (x - mean)^2 <= 2^30
-    const int32_t var = (int32_t)floor((double)cen / (double)p.cols); // < 2^15
-    int32_t sd = isqrt_newton10(var);
-    if (sd == 0) sd = 1;
-    const int32_t fs = (int32_t)floor((double)(1 << p.m) / (double)sd); // <= 2^22
+    const int32_t mean = floordiv_est(s1, p.cols, rcols);          // in [-128, 127]
+    const int32_t cen = s2 - 2 * mean * s1 + p.cols * mean * mean; // sum (x - mean)^2 <= 2^30
+    const int32_t var = floordiv_est(cen, p.cols, rcols);          // < 2^15
+    const int32_t sd = var > 0 ? isqrt_newton10_fast(var, p.sqmask) : 1;
+    const int32_t fs = floordiv_est(1 << p.m, sd, __builtin_amdgcn_rcpf((float)sd));  // <= 2^22
     const int32_t mfs = mean * fs;
-    const int32_t sh = p.m - p.f;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int col = 16 * (gl + G * k);
-      const int cl = col < p.cols ? col : 0;  // LDS copy: stay inside it
       v4i o;
-      v4i gk, bk[4];
-      if constexpr (REGS) {
-        gk = gam[k];
+      v4i gk[4], bk[4];  // gamma (int32) and beta of the chunk's 16 columns
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bk[j] = bet[k][j];
-      } else {
-        gk = reinterpret_cast<const v4i*>(ln_aff + p.cols)[cl / 16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bk[j] = reinterpret_cast<const v4i*>(ln_aff)[cl / 4 + j];
+      for (int j = 0; j < 4; ++j) {
+        bk[j] = reinterpret_cast<const v4i*>(ln_aff)[(k * 4 + j) * G + gl];
+        gk[j] = reinterpret_cast<const v4i*>(ln_aff)[NENT + (k * 4 + j) * G + gl];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int32_t w = d[k][j], g = gk[j];
+        const int32_t w = d[k][j];
         uint32_t res = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int32_t xv = (int8_t)(w >> (8 * i));  // signed byte i
-          const int32_t gv = (int8_t)(g >> (8 * i));
+          const int32_t gv = gk[j][i];
           // (x - mean) * fs with |x - mean| <= 255 and fs <= 2^22: fits 31 bits
           const int32_t nrm = (__mul24(xv, fs) - mfs) >> sh;  // |nrm| <= 2^16
           const int32_t bv = bk[j][i];
           int32_t y;
-          if constexpr (FAST) {
-            const int32_t ys = __builtin_elementwise_add_sat(__mul24(nrm, gv), bv);
+          if constexpr (RQ == RQ_WIN) {
+            const int32_t ys = mad24_sat(nrm, gv, bv);
+            const int32_t yc = med3_i32(ys, nywin, p.ywin);
+            y = clamp127(__mul24(yc, p.b) >> p.c);
+          } else if constexpr (RQ == RQ_MULHI) {
+            const int32_t ys = mad24_sat(nrm, gv, bv);
             y = clamp127(__mulhi(ys, p.bm));
           } else {
             const int64_t yl = (int64_t)__mul24(nrm, gv) + bv;
@@ -301,7 +377,10 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
         o[j] = (int32_t)res;
       }
       if (rv && col < p.cols) __builtin_amdgcn_raw_buffer_store_b128(o, orr, row * p.cols + col, 0, 0);
+      // one chunk's gamma/beta reads at a time: keeps the register count low
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (r0 + step < p.rows) load_rows(r0 + step, d);
   }
 }
 
@@ -328,14 +407,15 @@ template <int G, int NCH>
 void* gelu_ptr() { return (void*)&iqgelu_fwd<G, NCH>; }
 
 template <int G, int NCH>
-void* ln_ptr(bool fast) {
-  return fast ? (void*)&iqln_fwd<G, NCH, true> : (void*)&iqln_fwd<G, NCH, false>;
+void* ln_ptr(int rq) {
+  return rq == RQ_WIN ? (void*)&iqln_fwd<G, NCH, RQ_WIN>
+       : rq == RQ_MULHI ? (void*)&iqln_fwd<G, NCH, RQ_MULHI> : (void*)&iqln_fwd<G, NCH, RQ_WIDE>;
 }
 
 template <bool LN>
-void* pick_kernel(Shape s, bool fast) {
+void* pick_kernel(Shape s, int rq) {
 #define IQB_CASE(GG, NN) \
-  if (s.g == GG && s.nch == NN) return LN ? ln_ptr<GG, NN>(fast) : gelu_ptr<GG, NN>();
+  if (s.g == GG && s.nch == NN) return LN ? ln_ptr<GG, NN>(rq) : gelu_ptr<GG, NN>();
   IQB_CASE(16, 1) IQB_CASE(16, 2) IQB_CASE(16, 3) IQB_CASE(16, 4)
   IQB_CASE(16, 5) IQB_CASE(16, 6) IQB_CASE(16, 7) IQB_CASE(16, 8)
   IQB_CASE(64, 3) IQB_CASE(64, 4) IQB_CASE(64, 6) IQB_CASE(64, 8) IQB_CASE(64, 12) IQB_CASE(64, 16)
@@ -343,12 +423,11 @@ void* pick_kernel(Shape s, bool fast) {
   return nullptr;
 }
 
-int check_device(int* dev, int* cus) {
+int check_device(int* dev) {
   hipDeviceProp_t prop;
   if (hipGetDevice(dev) != hipSuccess || hipGetDeviceProperties(&prop, *dev) != hipSuccess)
     return IQATTN_E_DEVICE;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return IQATTN_E_DEVICE;
-  *cus = prop.multiProcessorCount;
   return IQATTN_OK;
 }
 
@@ -358,10 +437,14 @@ int check_rows_cols(int32_t rows, int32_t cols) {
   return IQATTN_OK;
 }
 
-unsigned grid_for(int32_t rows, int rows_per_block, int cus, int per_cu) {
+// One block per group of rows; the hardware hands the blocks to the CUs as
+// earlier ones finish (measured faster here than persistent blocks looping
+// over the groups, for both kernels).  The kernels still loop when the grid
+// is capped.
+unsigned grid_for(int32_t rows, int rows_per_block) {
   const int64_t need = ((int64_t)rows + rows_per_block - 1) / rows_per_block;
-  const int64_t cap = (int64_t)cus * per_cu;
-  return (unsigned)(need < cap ? need : cap);
+  const int64_t cap = (int64_t)1 << 30;
+  return (unsigned)(need < 1 ? 1 : (need > cap ? cap : need));
 }
 
 }  // namespace
@@ -395,17 +478,17 @@ extern "C" int iqgelu_create(const iqgelu_params* p, iqgelu_ctx** out) {
       p->k_out < 2 || p->k_out > 8 || p->intdiv_m < p->k_out - 1 || p->intdiv_m > 40 ||
       p->b < 1 || p->c < 0 || p->c > 62)
     return IQATTN_E_INVAL;
-  int dev = 0, cus = 0;
-  if ((rc = check_device(&dev, &cus))) return rc;
+  int dev = 0;
+  if ((rc = check_device(&dev))) return rc;
   const Shape s = pick_shape(p->cols);
-  void* k = pick_kernel<false>(s, false);
+  void* k = pick_kernel<false>(s, 0);
   if (!k) return IQATTN_E_SHAPE;
   iqgelu_ctx* c = (iqgelu_ctx*)calloc(1, sizeof(iqgelu_ctx));
   if (!c) return IQATTN_E_ALLOC;
   c->device = dev;
   c->kernel = k;
   const int rpb = (64 / s.g) * (kGeluThreads / 64);
-  c->grid = grid_for(p->rows, rpb, cus, 2);  // 2 x 32 KiB of table per CU
+  c->grid = grid_for(p->rows, rpb);
   if (hipMalloc((void**)&c->tab, kTabBytes) != hipSuccess) {
     free(c);
     return IQATTN_E_ALLOC;
@@ -457,40 +540,46 @@ extern "C" int iqlayernorm_create(const iqlayernorm_params* p, iqlayernorm_ctx**
   if (p->norm_frac_bits < 0 || p->norm_frac_bits > 8 || p->intdiv_m < p->norm_frac_bits ||
       p->intdiv_m > 22 || p->b < 1 || p->c < 0 || p->c > 62)
     return IQATTN_E_INVAL;
-  int dev = 0, cus = 0;
-  if ((rc = check_device(&dev, &cus))) return rc;
-  // Fast requantisation: clip(floor(b y / 2^c)) = clip(mulhi(y, b << (32 - c)))
-  // for int32 y when b << (32 - c) < 2^31; y = nrm * gamma + beta may leave
-  // int32, so it saturates, which keeps the clipped result exact when
-  // (2^31 - 1) b / 2^c >= 128 (a saturated y clips to +-127 either way).
-  bool fast = false;
-  int32_t bm = 0;
-  if (p->c >= 1 && p->c <= 32) {
+  int dev = 0;
+  if ((rc = check_device(&dev))) return rc;
+  // The requantisation form: RQ_WIN when b, ywin < 2^23 and 127 * 2^c + b <
+  // 2^31; else RQ_MULHI when b << (32 - c) < 2^31 and (2^31 - 1) b / 2^c >= 128
+  // (a saturated y clips either way); else the 64-bit form.
+  int rq = RQ_WIDE;
+  int32_t bm = 0, ywin = 0;
+  if (p->c <= 31) {
+    const int64_t yw = (((int64_t)127 << p->c) + p->b - 1) / p->b;
+    if (p->b < (1 << 23) && yw < (1 << 23) && ((int64_t)127 << p->c) + p->b < ((int64_t)1 << 31)) {
+      rq = RQ_WIN;
+      ywin = (int32_t)yw;
+    }
+  }
+  if (rq == RQ_WIDE && p->c >= 1 && p->c <= 32) {
     const int64_t v = (int64_t)p->b << (32 - p->c);
     const bool sat_ok = (((int64_t)INT32_MAX * p->b) >> p->c) >= 128;
     if (v < ((int64_t)1 << 31) && sat_ok) {
-      fast = true;
+      rq = RQ_MULHI;
       bm = (int32_t)v;
     }
   }
   const Shape s = pick_shape(p->cols);
-  void* k = pick_kernel<true>(s, fast);
+  void* k = pick_kernel<true>(s, rq);
   if (!k) return IQATTN_E_SHAPE;
   iqlayernorm_ctx* c = (iqlayernorm_ctx*)calloc(1, sizeof(iqlayernorm_ctx));
   if (!c) return IQATTN_E_ALLOC;
   c->device = dev;
   c->kernel = k;
   const int rpb = (64 / s.g) * (kLnThreads / 64);
-  c->grid = grid_for(p->rows, rpb, cus, 8);
-  c->lds_bytes = ln_affine_in_regs(s.nch) ? 0u : (unsigned)p->cols * 5u;
+  c->lds_bytes = (unsigned)(128 * s.g * s.nch);
   if (c->lds_bytes > 65536u) {
-    // a block may hold at most 64 KiB of LDS
+    // more than 64 KiB of dynamic LDS needs the kernel to opt in
     if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->lds_bytes) !=
         hipSuccess) {
       free(c);
       return IQATTN_E_DEVICE;
     }
   }
+  c->grid = grid_for(p->rows, rpb);
   LnDev& d = c->dp;
   d.rows = p->rows;
   d.cols = p->cols;
@@ -499,6 +588,26 @@ extern "C" int iqlayernorm_create(const iqlayernorm_params* p, iqlayernorm_ctx**
   d.b = p->b;
   d.c = p->c;
   d.bm = bm;
+  d.ywin = ywin;
+  {
+    uint8_t* flags = NULL;
+    uint8_t host[192];
+    hipError_t e = hipMalloc((void**)&flags, sizeof(host));
+    if (e != hipSuccess) {
+      free(c);
+      return IQATTN_E_ALLOC;
+    }
+    hipLaunchKernelGGL(iqln_newton_flags, dim3(1), dim3(192), 0, 0, flags);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpy(host, flags, sizeof(host), hipMemcpyDeviceToHost);
+    (void)hipFree(flags);
+    if (e != hipSuccess) {
+      free(c);
+      return set_hip_error(e, "iqlayernorm newton flags");
+    }
+    for (int k = 0; k < 192; ++k)
+      if (host[k]) d.sqmask[k >> 5] |= 1u << (k & 31);
+  }
   *out = c;
   return IQATTN_OK;
 }

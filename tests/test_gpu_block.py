@@ -1,6 +1,6 @@
 """Bit-exact parity of ShiftGELU and I-LayerNorm (through the C-ABI) with the
-CPU oracle: every kernel shape (16 and 64 lanes a row, 1..16 chunks a lane,
-affine parameters in registers and in LDS), ragged row and column counts,
+CPU oracle: every kernel shape (16 and 64 lanes a row, 1..16 chunks a lane),
+ragged row and column counts,
 every (row maximum, x) pair of the ShiftGELU table, constant and extreme rows,
 both requantisation paths, and the ViT-B shapes at full size."""
 import sys
@@ -200,3 +200,27 @@ def test_block_zero_rows_and_errors(torch_dev):
     assert lib.iqgelu_forward(C.c_void_p(g.ctx), None, C.c_void_p(x.data_ptr()),
                               None) == IQ.IQATTN_E_NULL
     g.close()
+
+
+@pytest.mark.parametrize("params", [FAST, SLOW], ids=["fast", "slow"])
+def test_layernorm_newton_oscillation_rows(torch_dev, params):
+    """Rows whose variance is k^2 - 1 for every k from 2 to 127 (the largest
+    variance an int8 row reaches is below 128^2): there the ten Newton steps
+    of the square root alternate between k - 1 and k, and the result is the
+    step the iteration stops on.  Row k holds 512 values +k, 511 values -k and
+    one -k + 1 (in a fixed shuffled order): sum 1, mean 0, sum of squares
+    1024 k^2 - 2k + 1."""
+    _say(f"layernorm newton rows {params}")
+    rng = np.random.default_rng(9)
+    rows = []
+    for k in range(2, 128):
+        r = np.array([k] * 512 + [-k] * 511 + [-k + 1], dtype=np.int64)
+        rows.append(r[rng.permutation(1024)])
+    x = np.array(rows, dtype=np.int8)
+    gamma = rng.integers(-128, 128, 1024).astype(np.int8)
+    beta = rng.integers(-20000, 20000, 1024).astype(np.int32)
+    _, st = oracle.ilayernorm(x, gamma, beta, params, dump=True)
+    assert list(st[:, 1]) == [k * k - 1 for k in range(2, 128)]
+    got = ln_gpu(torch_dev, x, gamma, beta, params)
+    want = oracle.ilayernorm(x, gamma, beta, params)
+    assert not _mismatch(got, want), _mismatch(got, want)
