@@ -313,3 +313,53 @@ def gelu_workload(name: str, seed: int = 3000) -> GeluWorkload:
 def layernorm_workload(name: str, seed: int = 4000) -> LayerNormWorkload:
     rows, cols = LAYERNORM_CONFIGS[name]
     return make_layernorm(rows, cols, seed, name=name)
+
+
+# ---------------------------------------------------------------- linear attention
+S_LQ, S_LK, S_LV, S_LAPARAMS = 19, 20, 21, 22
+
+
+def linattn_params(seed: int, seq_len: int, head_dim: int, sigma=24.0) -> Dict[str, int]:
+    """Dyadic pairs for the softmax-free linear attention, from the input
+    distribution only (sigma of Q, K, V; N tokens; d features):
+      KV entries have std ~ sqrt(N) * (sigma / sqrt 2) * sigma  -> int8 std ~ 32;
+      ks entries have mean ~ 0.4 * sigma * N                    -> int8 ~ 96;
+      num ~ sqrt(d) * (sigma / sqrt 2) * 32, den ~ d * 0.4 * sigma * 96, and the
+      output pair maps num / den to an int8 std of about 32.
+    Each b is uniform in [2^14, 2^15); each c the exponent that gives the target."""
+    import math
+    b = Stream(seed, S_LAPARAMS).randint(1 << 14, (1 << 15) - 1, 3)
+    half = sigma / math.sqrt(2.0)
+    kv_std = math.sqrt(seq_len) * half * sigma
+    ks_mean = 0.4 * sigma * seq_len
+    num_std = math.sqrt(head_dim) * half * 32.0
+    den = head_dim * 0.4 * sigma * 96.0
+    c_kv = max(0, round(math.log2(b[0] * kv_std / 32.0)))
+    c_ks = max(0, math.ceil(math.log2(b[1] * ks_mean / 96.0)))
+    c_out = max(0, round(math.log2(b[2] * num_std / (den * 32.0))))
+    return dict(kv_b=int(b[0]), kv_c=c_kv, ks_b=int(b[1]), ks_c=c_ks, out_b=int(b[2]), out_c=c_out)
+
+
+def make_linattn(batch: int, heads: int, seq_len: int, head_dim: int, seed: int, sigma=24.0,
+                 name: str = "custom") -> Workload:
+    shape = (batch, heads, seq_len, head_dim)
+    q = int8_gaussian(Stream(seed, S_LQ), shape, sigma)
+    k = int8_gaussian(Stream(seed, S_LK), shape, sigma)
+    v = int8_gaussian(Stream(seed, S_LV), shape, sigma)
+    return Workload(name, batch, heads, seq_len, head_dim, q, k, v,
+                    linattn_params(seed, seq_len, head_dim, sigma))
+
+
+# EfficientViT-style ReLU attention at stage 3 (16-pixel tokens): 224 px -> 196
+# tokens, 512 px -> 1024 tokens; head dim 16 (B1-like) and 32 (B3-like), the
+# heads doubled by the multi-scale branch.
+LINATTN_CONFIGS = {
+    "effvit_b64_h16_n196_d16": (64, 16, 196, 16),
+    "effvit_b64_h16_n1024_d16": (64, 16, 1024, 16),
+    "effvit_b16_h32_n1024_d32": (16, 32, 1024, 32),
+}
+
+
+def linattn_workload(name: str, seed: int = 5000) -> Workload:
+    B, H, N, d = LINATTN_CONFIGS[name]
+    return make_linattn(B, H, N, d, seed, name=name)

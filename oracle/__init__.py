@@ -5,5 +5,5 @@ baseline import this package; the product path never does.
 """
 from .oracle import (  # noqa: F401
     build, forward, softmax_row, requant, requant_array, shift_exp, ilog2r,
-    check_params, library_path, linear, shiftgelu, isqrt10, ilayernorm,
+    check_params, library_path, linear, shiftgelu, isqrt10, ilayernorm, linattn,
 )

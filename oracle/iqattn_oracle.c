@@ -355,3 +355,89 @@ int orc_ilayernorm(const int8_t* x, const int8_t* gamma, const int32_t* beta, in
   }
   return 0;
 }
+
+/* ---------------------------------------------------------------- linear attention
+ * LA1 ReLU acts on the int8 codes: the symmetric quantiser's scale is positive,
+ *     so max(S q, 0) = S max(q, 0).
+ * LA2 The two sums over the tokens (steps i and ii of the page's five) are
+ *     integers on the scales S_K S_V and S_K; each is requantised to int8 by
+ *     its own dyadic pair before the products with ReLU(Q) (the page names a
+ *     scale of its own for the summed keys, so the sum is a quantised tensor;
+ *     KV is taken the same way).
+ * LA3 The divisor X = ReLU(Q_i) . ksq (step iv) is an integer >= 0; its log2
+ *     is the leading-one index plus the next lower bit (Eq. 11, the rule the
+ *     page cites), the same ilog2r as the LIS codes.  The constant
+ *     log2(S_Q S_ks) of Eq. 11 is folded into the output pair (out_b, out_c).
+ * LA4 The division (step v) is the shift by that code, after the output
+ *     multiplier: out = clip((out_b num) >> (out_c + L), -127, 127), floor
+ *     semantics; the clip (-a, b) of Eq. 11 is not reached by codes of int32
+ *     divisors (L in [0, 32]).
+ * LA5 A divisor of 0 (ReLU(Q_i) = 0, or ksq = 0 where Q_i is positive) makes
+ *     every numerator 0 as well; the code is taken as 0 and the output is 0.
+ * LA6 No 1/sqrt(d) or other scaling: the ReLU similarity has none.          */
+int orc_linattn(const orc_linattn_params* p, const int8_t* q, const int8_t* k, const int8_t* v,
+                int8_t* out, int64_t head_begin, int64_t head_end, int64_t* dump) {
+  if (!p || p->batch < 0 || p->heads < 1 || p->seq_len < 1 || p->head_dim < 1 ||
+      p->head_dim > 1024)
+    return -1;
+  const int32_t bs[3] = {p->kv_b, p->ks_b, p->out_b}, cs[3] = {p->kv_c, p->ks_c, p->out_c};
+  for (int i = 0; i < 3; ++i)
+    if (bs[i] < 1 || cs[i] < 0 || cs[i] > 62) return -1;
+  const int64_t NH = p->batch * p->heads, N = p->seq_len, d = p->head_dim;
+  if (head_begin < 0 || head_end > NH || head_begin > head_end) return -1;
+  int64_t* kv = (int64_t*)malloc((size_t)(d * d + d) * sizeof(int64_t));
+  int64_t* num = (int64_t*)malloc((size_t)d * sizeof(int64_t));
+  if (!kv || !num) {
+    free(kv);
+    free(num);
+    return -1;
+  }
+  int64_t* ks = kv + d * d;
+  for (int64_t hh = head_begin; hh < head_end; ++hh) {
+    const int8_t* Q = q + hh * N * d;
+    const int8_t* K = k + hh * N * d;
+    const int8_t* V = v + hh * N * d;
+    /* steps i and ii, then LA2 */
+    for (int64_t a = 0; a < d; ++a) {
+      int64_t sk = 0;
+      for (int64_t j = 0; j < N; ++j) sk += K[j * d + a] > 0 ? K[j * d + a] : 0;
+      ks[a] = orc_requant(sk, p->ks_b, p->ks_c);
+      for (int64_t b = 0; b < d; ++b) {
+        int64_t acc = 0;
+        for (int64_t j = 0; j < N; ++j) {
+          const int64_t kr = K[j * d + a] > 0 ? K[j * d + a] : 0;
+          acc += kr * V[j * d + b];
+        }
+        kv[a * d + b] = orc_requant(acc, p->kv_b, p->kv_c);
+      }
+    }
+    if (dump)
+      for (int64_t t = 0; t < d * d + d; ++t) dump[(hh - head_begin) * (d * d + d) + t] = kv[t];
+    /* steps iii, iv, v */
+    for (int64_t i = 0; i < N; ++i) {
+      int64_t den = 0;
+      for (int64_t a = 0; a < d; ++a) {
+        const int64_t qr = Q[i * d + a] > 0 ? Q[i * d + a] : 0;
+        den += qr * ks[a];
+      }
+      for (int64_t b = 0; b < d; ++b) {
+        int64_t acc = 0;
+        for (int64_t a = 0; a < d; ++a) {
+          const int64_t qr = Q[i * d + a] > 0 ? Q[i * d + a] : 0;
+          acc += qr * kv[a * d + b];
+        }
+        num[b] = acc;
+      }
+      const int64_t L = den > 0 ? orc_ilog2r(den) : 0; /* LA3, LA5 */
+      for (int64_t b = 0; b < d; ++b) {
+        const int64_t sh = p->out_c + L;
+        const int64_t prod = (int64_t)p->out_b * num[b];
+        const int64_t y = sh >= 63 ? (prod < 0 ? -1 : 0) : floor_div(prod, pow2(sh));
+        out[hh * N * d + i * d + b] = (int8_t)clip64(y, -127, 127);
+      }
+    }
+  }
+  free(kv);
+  free(num);
+  return 0;
+}

@@ -28,10 +28,14 @@
  *   I-ViT sec. 3.4 "Integer-only GELU: ShiftGELU" and sec. 3.5 "Integer-only
  *     LayerNorm: I-LayerNorm" for the two element-wise/row-wise operators
  *     around the attention (orc_shiftgelu, orc_ilayernorm).
+ *   Trio-ViT (cloud.tencent.com article), sec. III "Structure of EfficientViT"
+ *     Eq. 4, sec. IV "Log2 Quantization for Divisors in MSAs" Eq. 11 and
+ *     sec. V "Distinct Computational Pattern of Attention" (steps i-v) for the
+ *     softmax-free linear attention (orc_linattn).
  *
  * Readings taken where the pages are silent, garbled or ambiguous are listed
  * next to the code that takes them (R1..R22, G1..G3, L1..L4 in the comments of
- * the .c file).
+ * the .c file; LA1..LA6 for the linear attention).
  * Parity unpinned: the readings themselves (I0 = 1/S_logit, the extra exponent
  * fraction bits n, M, the clamp of P at 2^(k_out-1)-1, floor requantisation,
  * bias added to the int32 accumulator, the midpoint of the log2 rounding, the
@@ -123,6 +127,28 @@ int64_t orc_isqrt10(int64_t v);
 int orc_ilayernorm(const int8_t* x, const int8_t* gamma, const int32_t* beta, int64_t rows,
                    int64_t cols, int32_t norm_frac_bits, int32_t intdiv_m, int32_t b, int32_t c,
                    int8_t* out, int64_t row_begin, int64_t row_end, int64_t* stat_dump);
+
+/* Softmax-free integer linear attention (Trio-ViT, cloud.tencent.com article:
+ * EfficientViT's ReLU global attention, Eq. 4; log2 quantisation of the
+ * divisor, Eq. 11, with the leading-one detector and shift division) on one
+ * batch of int8 Q, K, V [batch][heads][seq_len][head_dim]:
+ *   Qr = max(Q, 0), Kr = max(K, 0)                                  (LA1)
+ *   KV[a][b] = sum_j Kr[j][a] V[j][b],  ks[a] = sum_j Kr[j][a]        int64
+ *   KVq = clip((kv_b KV) >> kv_c, -127, 127), ksq = clip((ks_b ks) >> ks_c,
+ *         -127, 127)                                                (LA2)
+ *   num[i][b] = sum_a Qr[i][a] KVq[a][b],  den[i] = sum_a Qr[i][a] ksq[a]
+ *   L[i] = ilog2r(den[i]) (0 when den[i] = 0)                       (LA3, LA5)
+ *   out[i][b] = clip((out_b num[i][b]) >> (out_c + L[i]), -127, 127)  (LA4)
+ * Heads [head_begin, head_end) of the flattened batch * heads are written;
+ * dump, when not NULL, receives per head (KVq [d][d], ksq [d]) as int64
+ * [heads][d * d + d].  Returns 0, or -1 for out-of-range arguments.          */
+typedef struct orc_linattn_params {
+  int64_t batch, heads, seq_len, head_dim;
+  int32_t kv_b, kv_c, ks_b, ks_c, out_b, out_c;
+} orc_linattn_params;
+
+int orc_linattn(const orc_linattn_params* p, const int8_t* q, const int8_t* k, const int8_t* v,
+                int8_t* out, int64_t head_begin, int64_t head_end, int64_t* dump);
 
 /* Steps exposed one at a time for the tests. */
 int32_t orc_requant(int64_t x, int32_t b, int32_t c);

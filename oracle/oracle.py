@@ -71,6 +71,8 @@ def _load():
                                        C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                        C.c_int64, C.c_int64, C.c_void_p]
         lib.orc_ilayernorm.restype = C.c_int
+        lib.orc_linattn.argtypes = [C.c_void_p] * 5 + [C.c_int64, C.c_int64, C.c_void_p]
+        lib.orc_linattn.restype = C.c_int
         lib.orc_requant.restype = C.c_int32
         lib.orc_requant_array.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32,
                                           C.c_void_p]
@@ -243,3 +245,29 @@ def ilayernorm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, params: Dict[
     if rc != 0:
         raise ValueError(f"orc_ilayernorm: invalid arguments ({rc})")
     return (out[r0:r1], st[r0:r1]) if dump else out[r0:r1]
+
+
+class _LinattnParams(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("batch", "heads", "seq_len", "head_dim")] + \
+        [(n, C.c_int32) for n in ("kv_b", "kv_c", "ks_b", "ks_c", "out_b", "out_c")]
+
+
+def linattn(q: np.ndarray, k: np.ndarray, v: np.ndarray, params: Dict[str, int], heads=None,
+            dump=False):
+    """Softmax-free integer linear attention of int8 Q, K, V [B, H, N, d] -> int8
+    [B, H, N, d] (and, with dump, the int64 requantised KV [d, d] and ks [d] per
+    head, shaped [B * H, d * d + d]).  heads = (begin, end) over the flattened
+    B * H limits the heads computed; the others stay 0."""
+    lib = _load()
+    q, k, v = (np.ascontiguousarray(t, dtype=np.int8) for t in (q, k, v))
+    B, H, N, d = q.shape
+    pp = _LinattnParams(B, H, N, d, *(int(params[n]) for n in
+                                     ("kv_b", "kv_c", "ks_b", "ks_c", "out_b", "out_c")))
+    h0, h1 = (0, B * H) if heads is None else heads
+    out = np.zeros(q.shape, np.int8)
+    dm = np.zeros((max(h1 - h0, 0), d * d + d), np.int64) if dump else None
+    rc = lib.orc_linattn(C.addressof(pp), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                         out.ctypes.data, h0, h1, dm.ctypes.data if dump else None)
+    if rc != 0:
+        raise ValueError(f"orc_linattn: invalid arguments ({rc})")
+    return (out, dm) if dump else out

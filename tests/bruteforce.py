@@ -103,3 +103,23 @@ def ilayernorm_row(xs, gamma, beta, p):
     fs = fl(2 ** m, sd)
     return [requant(fl((x - mean) * fs, 2 ** (m - f)) * int(g) + int(bt), p["b"], p["c"])
             for x, g, bt in zip(xs, gamma, beta)]
+
+
+def linattn_head(Q, K, V, p):
+    """Softmax-free linear attention of one head: Q, K, V nested [N][d] ints."""
+    N, d = len(Q), len(Q[0])
+    relu = lambda x: x if x > 0 else 0  # noqa: E731
+    kvq = [[requant(sum(relu(K[j][a]) * V[j][b] for j in range(N)), p["kv_b"], p["kv_c"])
+            for b in range(d)] for a in range(d)]
+    ksq = [requant(sum(relu(K[j][a]) for j in range(N)), p["ks_b"], p["ks_c"]) for a in range(d)]
+    out = []
+    for i in range(N):
+        qr = [relu(x) for x in Q[i]]
+        den = sum(qr[a] * ksq[a] for a in range(d))
+        L = ilog2r(den) if den > 0 else 0
+        row = []
+        for b in range(d):
+            num = sum(qr[a] * kvq[a][b] for a in range(d))
+            row.append(max(-127, min(127, fl(p["out_b"] * num, 2 ** (p["out_c"] + L)))))
+        out.append(row)
+    return out
