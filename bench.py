@@ -221,6 +221,67 @@ def bench_block(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_linattn(args):
+    """Time the softmax-free integer linear attention on an EfficientViT-style
+    shape; roofline against HBM (Q, K, V read once, Out written once)."""
+    import torch
+    from integer_only_quantized_int8_amd import workloads as W
+    from integer_only_quantized_int8_amd.iqattn import IQLinAttn
+    wl = W.linattn_workload(args.linattn)
+    B, H, N, d = wl.q.shape
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(t).to(dev) for t in (wl.q, wl.k, wl.v))
+    out = torch.empty_like(q)
+    op = IQLinAttn(wl.q.shape, wl.params)
+    for _ in range(args.warmup):
+        op.forward(q, k, v, out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            op.forward(q, k, v, out)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_ms = g0.elapsed_time(g1) / args.steps
+    heads = B * H
+    algo = float(4 * N * d * heads)
+    ops = 4.0 * N * d * d * heads  # the two int8 contractions, 2 N d^2 each
+    gbs = algo / (kern_ms * 1e-3) / 1e9
+    res = {"metric": f"integer-only linear attention int8 TOPS, {wl.name}",
+           "value": round(ops / (step_ms * 1e-3) / 1e12, 3), "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+           "data": "synthetic (seeded int8 Q, K, V)",
+           "config": {"workload": wl.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d},
+           "kernel_us_mean": round(kern_ms * 1e3, 3),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": int(algo)}}
+    if not args.no_cpu:
+        import oracle
+        passes, t1 = 0, time.perf_counter()
+        while True:  # whole passes over every head, about 2 s of CPU time
+            oracle.linattn(wl.q, wl.k, wl.v, wl.params)
+            passes += 1
+            cpu_s = time.perf_counter() - t1
+            if cpu_s >= 2.0:
+                break
+        res["cpu_baseline"] = {"value": round(ops * passes / cpu_s / 1e12, 6),
+                               "unit": "TOPS", "cores": 1, "kind": "oracle",
+                               "sample": f"{passes} whole pass(es) over the {heads} heads, "
+                                         f"{cpu_s:.2f} s single-threaded C -O2 on {cpu_model()}"}
+    op.close()
+    print(json.dumps(res), flush=True)
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -245,6 +306,8 @@ def main():
     ap.add_argument("--linear", default=None,
                     help="time an int8 linear layer instead (workload name from "
                          "workloads.LINEAR_CONFIGS, e.g. vitb_qkv_b128_n197_c768)")
+    ap.add_argument("--linattn", default=None,
+                    help="time the softmax-free linear attention on this EfficientViT-style shape")
     ap.add_argument("--block", default=None, choices=("gelu", "layernorm"),
                     help="time ShiftGELU or I-LayerNorm on the ViT-B shapes instead")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -279,6 +342,9 @@ def main():
         return
     if args.block:
         bench_block(args)
+        return
+    if args.linattn:
+        bench_linattn(args)
         return
 
     t0 = time.time()

@@ -36,7 +36,8 @@ IQLINEAR_QKV_HEADS = 1
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
             "iqlinear_create", "iqlinear_forward", "iqlinear_destroy",
             "iqgelu_create", "iqgelu_forward", "iqgelu_destroy",
-            "iqlayernorm_create", "iqlayernorm_forward", "iqlayernorm_destroy")
+            "iqlayernorm_create", "iqlayernorm_forward", "iqlayernorm_destroy",
+            "iqlinattn_create", "iqlinattn_forward", "iqlinattn_destroy")
 
 
 class iqattn_params(C.Structure):
@@ -60,6 +61,12 @@ class iqgelu_params(C.Structure):
 class iqlayernorm_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "rows", "cols", "norm_frac_bits", "intdiv_m", "b", "c")]
+
+
+class iqlinattn_params(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "batch", "heads", "seq_len", "head_dim", "kv_b", "kv_c", "ks_b", "ks_c", "out_b",
+        "out_c")]
 
 
 class IQAttnError(RuntimeError):
@@ -105,6 +112,12 @@ def load_library():
         lib.iqlayernorm_forward.restype = C.c_int
         lib.iqlayernorm_destroy.argtypes = [C.c_void_p]
         lib.iqlayernorm_destroy.restype = C.c_int
+        lib.iqlinattn_create.argtypes = [C.POINTER(iqlinattn_params), C.POINTER(C.c_void_p)]
+        lib.iqlinattn_create.restype = C.c_int
+        lib.iqlinattn_forward.argtypes = [C.c_void_p] * 6
+        lib.iqlinattn_forward.restype = C.c_int
+        lib.iqlinattn_destroy.argtypes = [C.c_void_p]
+        lib.iqlinattn_destroy.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -401,6 +414,54 @@ class IQLayerNorm(_Owner):
                                                       device=x.device)
         _check("out", out, torch.int8, (rows, cols))
         iqlayernorm_forward(self.ctx, x, gamma, beta, out, stream)
+        return out
+
+    __call__ = forward
+
+
+# ---------------------------------------------------------------- linear attention
+def make_linattn_params(shape, params: Dict[str, object]) -> iqlinattn_params:
+    B, H, N, d = shape
+    return _fill(iqlinattn_params, ("batch", "heads", "seq_len", "head_dim", "kv_b", "kv_c",
+                                    "ks_b", "ks_c", "out_b", "out_c"),
+                 dict(params, batch=B, heads=H, seq_len=N, head_dim=d))
+
+
+def iqlinattn_create(p: iqlinattn_params) -> int:
+    return _create(load_library().iqlinattn_create, p, "iqlinattn_create")
+
+
+def iqlinattn_forward(ctx: int, q, k, v, out, stream=None) -> None:
+    ptr = lambda t: None if t is None else C.c_void_p(t.data_ptr())  # noqa: E731
+    rc = load_library().iqlinattn_forward(C.c_void_p(ctx), ptr(q), ptr(k), ptr(v), ptr(out),
+                                          C.c_void_p(_stream_handle(stream)))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinattn_forward")
+
+
+def iqlinattn_destroy(ctx: Optional[int]) -> None:
+    rc = load_library().iqlinattn_destroy(C.c_void_p(ctx) if ctx else None)
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinattn_destroy")
+
+
+class IQLinAttn(_Owner):
+    """Owns one softmax-free linear-attention context: Q, K, V [B, H, N, d] int8."""
+    _destroy = staticmethod(iqlinattn_destroy)
+
+    def __init__(self, shape, params: Dict[str, object]):
+        self.shape = tuple(int(x) for x in shape)
+        self.params = dict(params)
+        self.ctx = iqlinattn_create(make_linattn_params(self.shape, self.params))
+
+    def forward(self, q, k, v, out=None, stream=None):
+        import torch
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _check(name, t, torch.int8, self.shape)
+        out = out if out is not None else torch.empty(self.shape, dtype=torch.int8,
+                                                      device=q.device)
+        _check("out", out, torch.int8, self.shape)
+        iqlinattn_forward(self.ctx, q, k, v, out, stream)
         return out
 
     __call__ = forward

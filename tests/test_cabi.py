@@ -19,7 +19,7 @@ def _declared_functions():
         if fn.endswith(".h"):
             text = open(os.path.join(ROOT, "include", fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(iq(?:attn|linear|gelu|layernorm)_\w+)\s*\(", text))
+            names |= set(re.findall(r"\b(iq(?:attn|linear|gelu|layernorm|linattn)_\w+)\s*\(", text))
     return names
 
 
@@ -193,3 +193,34 @@ def test_block_null_arguments(lib):
     assert lib.iqlayernorm_create(None, None) == IQ.IQATTN_E_NULL
     assert lib.iqlayernorm_destroy(None) == IQ.IQATTN_OK
     assert lib.iqlayernorm_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL
+
+
+def _la_rc(lib, **over):
+    p = dict(batch=2, heads=3, seq_len=40, head_dim=16, kv_b=20000, kv_c=20, ks_b=20000,
+             ks_c=12, out_b=20000, out_c=8)
+    p.update(over)
+    shape = (p.pop("batch"), p.pop("heads"), p.pop("seq_len"), p.pop("head_dim"))
+    ctx = C.c_void_p(12345)
+    rc = lib.iqlinattn_create(C.byref(IQ.make_linattn_params(shape, p)), C.byref(ctx))
+    return rc, ctx.value
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=-1), IQ.IQATTN_E_SHAPE), (dict(heads=0), IQ.IQATTN_E_SHAPE),
+    (dict(seq_len=0), IQ.IQATTN_E_SHAPE), (dict(seq_len=65537), IQ.IQATTN_E_SHAPE),
+    (dict(head_dim=8), IQ.IQATTN_E_SHAPE), (dict(head_dim=48), IQ.IQATTN_E_SHAPE),
+    (dict(head_dim=128), IQ.IQATTN_E_SHAPE),
+    (dict(batch=1024, heads=64, seq_len=1024, head_dim=64), IQ.IQATTN_E_SHAPE),
+    (dict(kv_b=0), IQ.IQATTN_E_INVAL), (dict(ks_c=63), IQ.IQATTN_E_INVAL),
+    (dict(out_c=-1), IQ.IQATTN_E_INVAL), (dict(out_b=0), IQ.IQATTN_E_INVAL),
+])
+def test_linattn_create_rejects_bad_parameters_before_any_device_call(lib, over, code):
+    rc, ctx = _la_rc(lib, **over)
+    assert rc == code
+    assert ctx is None
+
+
+def test_linattn_null_arguments(lib):
+    assert lib.iqlinattn_create(None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqlinattn_destroy(None) == IQ.IQATTN_OK
+    assert lib.iqlinattn_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL
