@@ -6,18 +6,19 @@
 // Attention" (steps i-v), sec. IV Eq. 11 (leading-one log2 of the divisor);
 // I-ViT (mer.run summary) sec. 3.2 (dyadic requantisation).
 //
-// One workgroup of 4 waves per head; the head's Q, K, V and Out are each read
+// One workgroup of 8 waves per head; the head's Q, K, V and Out are each read
 // or written once (4 N d bytes per head), so the kernel is HBM-bound and both
 // contractions run on int8 MFMA (v_mfma_i32_16x16x32_i8):
 //   phase 1 (steps i, ii): each wave streams 32-token chunks of K and V
-//     through its own LDS slot (the next chunk is loaded into registers while
-//     the current one is used); ds_read_b64_tr_b8 turns the row-major chunk
+//     through its own LDS slot (two chunks in flight in registers, the first
+//     issued at kernel entry); ds_read_b64_tr_b8 turns the row-major chunk
 //     into the token-major MFMA operands, so that one MFMA per 16 x 16 tile of
 //     KV = ReLU(K)^T V sums 32 tokens; ks = sum ReLU(K) comes from v_dot4 on
 //     the same operand bytes.  ReLU acts on the operand bytes (a byte mask).
-//     The four waves add their partial sums into LDS, where they are
+//     The waves add their partial sums into LDS, where they are
 //     requantised to int8 (KVq stored transposed, [b][a]).
-//   phase 2 (steps iii-v): for 16 tokens at a time, num^T = KVq^T . ReLU(Q)^T
+//   phase 2 (steps iii-v): for 16 tokens at a time (four tiles of Q in flight
+//     per wave, the first issued at kernel entry), num^T = KVq^T . ReLU(Q)^T
 //     by MFMA leaves each lane 4 consecutive output features of one token;
 //     den = ReLU(Q) . ksq by v_dot4 over the lane's operand bytes and a
 //     reduction over the lane groups; the output is
@@ -34,8 +35,14 @@
 namespace iqattn {
 namespace {
 
-constexpr int kLaThreads = 256;  // 4 waves
+#ifndef IQLA_WAVES
+#define IQLA_WAVES 8
+#endif
+constexpr int kLaWaves = IQLA_WAVES;
+constexpr int kLaThreads = 64 * kLaWaves;
 constexpr int kChunk = 32;       // tokens per MFMA step of the token sums
+constexpr int kKVDepth = 2;      // K/V chunks in flight per wave (phase 1)
+constexpr int kQDepth = 4;       // 16-token Q tiles in flight per wave (phase 2)
 
 struct LaParams {
   const int8_t* q;
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(kLaThreads) void iqlinattn_fwd(LaParams p) {
   constexpr int KS = (D + 31) / 32; // 32-feature k steps of the output product
   constexpr int PR = 32 * KS;       // row length of KVq^T and ksq in LDS (zero padded)
   constexpr int STG = 2 * kChunk * D;
-  __shared__ __attribute__((aligned(16))) int8_t stg[4][STG];
+  __shared__ __attribute__((aligned(16))) int8_t stg[kLaWaves][STG];
   __shared__ int32_t kv_acc[D * D];
   __shared__ int32_t ks_acc[D];
   __shared__ __attribute__((aligned(16))) int8_t kvq_t[D * PR];
@@ -131,13 +138,40 @@ __global__ __launch_bounds__(kLaThreads) void iqlinattn_fwd(LaParams p) {
   const __amdgpu_buffer_rsrc_t kr = buf_rsrc(p.k + hoff, hbytes);
   const __amdgpu_buffer_rsrc_t vr = buf_rsrc(p.v + hoff, hbytes);
   const __amdgpu_buffer_rsrc_t orr = buf_rsrc(p.out + hoff, hbytes);
+  const int nchunks = (p.n + kChunk - 1) / kChunk;
+  const int ntiles = (p.n + 15) / 16;
+
+  // ReLU(Q)^T operand bytes of tile t for this lane: token 16 t + m, features
+  // 32 s + 8 g .. (zero past D and, through the buffer bounds, past N)
+  auto load_q = [&](int t, int64_t (&qb)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qb[s] = 0;
+      if (32 * s + 8 * g < D) qb[s] = buf_load<int64_t>(qr, (16 * t + m) * D + 32 * s + 8 * g);
+    }
+  };
+  // the first Q tiles and K/V chunks of this wave load from the start, so that
+  // their latency overlaps the zeroing, the token sums and the reduction
+  int64_t qring[kQDepth][KS];
+#pragma unroll
+  for (int u = 0; u < kQDepth; ++u) {
+    const int t = wave + kLaWaves * u;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qring[u][s] = 0;
+    if (t < ntiles) load_q(t, qring[u]);
+  }
+  Stage<D> ring[kKVDepth];
+#pragma unroll
+  for (int u = 0; u < kKVDepth; ++u) {
+    const int c = wave + kLaWaves * u;
+    if (c < nchunks) ring[u].load(kr, vr, c, lane);
+  }
 
   for (int i = tid; i < D * D; i += kLaThreads) kv_acc[i] = 0;
   if (tid < D) ks_acc[tid] = 0;
   __syncthreads();
 
   // ---------------------------------------------------------------- phase 1
-  const int nchunks = (p.n + kChunk - 1) / kChunk;
   int8_t* my = stg[wave];
   // transposed-read address of this lane: token row 8 g + (m >> 1), bytes
   // 8 (m & 1) .. of the 16-feature tile
@@ -150,25 +184,27 @@ __global__ __launch_bounds__(kLaThreads) void iqlinattn_fwd(LaParams p) {
 #pragma unroll
     for (int b = 0; b < FT; ++b) acc[a][b] = v4i{0, 0, 0, 0};
   }
-  Stage<D> cur, nxt;
-  int c = wave;
-  if (c < nchunks) cur.load(kr, vr, c, lane);
-  for (; c < nchunks; c += 4) {
-    if (c + 4 < nchunks) nxt.load(kr, vr, c + 4, lane);
-    cur.store(my, lane);
-    int64_t ka[FT], vb[FT];
+  for (int c0 = wave; c0 < nchunks; c0 += kLaWaves * kKVDepth) {
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      ka[f] = relu8(read_tr8(my + tro + 16 * f));
-      vb[f] = read_tr8(my + kChunk * D + tro + 16 * f);
-      ksa[f] = __builtin_amdgcn_sdot4((int32_t)ka[f], 0x01010101, ksa[f], false);
-      ksa[f] = __builtin_amdgcn_sdot4((int32_t)(ka[f] >> 32), 0x01010101, ksa[f], false);
+    for (int u = 0; u < kKVDepth; ++u) {
+      const int c = c0 + kLaWaves * u;
+      if (c >= nchunks) break;
+      ring[u].store(my, lane);
+      const int cn = c + kLaWaves * kKVDepth;
+      if (cn < nchunks) ring[u].load(kr, vr, cn, lane);
+      int64_t ka[FT], vb[FT];
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        ka[f] = relu8(read_tr8(my + tro + 16 * f));
+        vb[f] = read_tr8(my + kChunk * D + tro + 16 * f);
+        ksa[f] = __builtin_amdgcn_sdot4((int32_t)ka[f], 0x01010101, ksa[f], false);
+        ksa[f] = __builtin_amdgcn_sdot4((int32_t)(ka[f] >> 32), 0x01010101, ksa[f], false);
+      }
+#pragma unroll
+      for (int a = 0; a < FT; ++a)
+#pragma unroll
+        for (int b = 0; b < FT; ++b) acc[a][b] = mfma32(ka[a], vb[b], acc[a][b]);
     }
-#pragma unroll
-    for (int a = 0; a < FT; ++a)
-#pragma unroll
-      for (int b = 0; b < FT; ++b) acc[a][b] = mfma32(ka[a], vb[b], acc[a][b]);
-    cur = nxt;
   }
   // lane (g, m): acc[a][b][r] = KV[16 a + 4 g + r][16 b + m]; ksa[a] sums the
   // tokens 8 g .. of feature 16 a + m
@@ -201,32 +237,37 @@ __global__ __launch_bounds__(kLaThreads) void iqlinattn_fwd(LaParams p) {
     for (int f = 0; f < FT; ++f)
       aop[f][s] = *reinterpret_cast<const int64_t*>(kvq_t + (16 * f + m) * PR + 32 * s + 8 * g);
   }
-  const int ntiles = (p.n + 15) / 16;
-  for (int t = wave; t < ntiles; t += 4) {
-    const int row = 16 * t + m;  // this lane's token (past N: zeros, no store)
-    int64_t qb[KS];
-    int32_t den = 0;
+  for (int t0 = wave; t0 < ntiles; t0 += kLaWaves * kQDepth) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qb[s] = 0;
-      if (32 * s + 8 * g < D) qb[s] = relu8(buf_load<int64_t>(qr, row * D + 32 * s + 8 * g));
-      den = __builtin_amdgcn_sdot4((int32_t)qb[s], (int32_t)kq[s], den, false);
-      den = __builtin_amdgcn_sdot4((int32_t)(qb[s] >> 32), (int32_t)(kq[s] >> 32), den, false);
-    }
-    den += __shfl_xor(den, 16, 64);
-    den += __shfl_xor(den, 32, 64);
-    const int32_t L = den > 0 ? ilog2r_dev((uint32_t)den) : 0;
-    const int32_t sh = p.out_c + L;
+    for (int u = 0; u < kQDepth; ++u) {
+      const int t = t0 + kLaWaves * u;
+      if (t >= ntiles) break;
+      const int row = 16 * t + m;  // this lane's token (past N: zeros, no store)
+      int64_t qb[KS];
+      int32_t den = 0;
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      v4i num = v4i{0, 0, 0, 0};
+      for (int s = 0; s < KS; ++s) {
+        qb[s] = relu8(qring[u][s]);
+        den = __builtin_amdgcn_sdot4((int32_t)qb[s], (int32_t)kq[s], den, false);
+        den = __builtin_amdgcn_sdot4((int32_t)(qb[s] >> 32), (int32_t)(kq[s] >> 32), den, false);
+      }
+      const int tn = t + kLaWaves * kQDepth;
+      if (tn < ntiles) load_q(tn, qring[u]);
+      den += __shfl_xor(den, 16, 64);
+      den += __shfl_xor(den, 32, 64);
+      const int32_t L = den > 0 ? ilog2r_dev((uint32_t)den) : 0;
+      const int32_t sh = p.out_c + L;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) num = mfma32(aop[f][s], qb[s], num);
-      // num[r] = numerator of feature 16 f + 4 g + r of token `row`
-      const uint32_t word = pack4_lowbytes(
-          (uint32_t)requant64(num[0], p.out_b, sh), (uint32_t)requant64(num[1], p.out_b, sh),
-          (uint32_t)requant64(num[2], p.out_b, sh), (uint32_t)requant64(num[3], p.out_b, sh));
-      __builtin_amdgcn_raw_buffer_store_b32(word, orr, row * D + 16 * f + 4 * g, 0, 0);
+      for (int f = 0; f < FT; ++f) {
+        v4i num = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) num = mfma32(aop[f][s], qb[s], num);
+        // num[r] = numerator of feature 16 f + 4 g + r of token `row`
+        const uint32_t word = pack4_lowbytes(
+            (uint32_t)requant64(num[0], p.out_b, sh), (uint32_t)requant64(num[1], p.out_b, sh),
+            (uint32_t)requant64(num[2], p.out_b, sh), (uint32_t)requant64(num[3], p.out_b, sh));
+        __builtin_amdgcn_raw_buffer_store_b32(word, orr, row * D + 16 * f + 4 * g, 0, 0);
+      }
     }
   }
 }
