@@ -39,8 +39,10 @@ METRIC = "integer-only MSA int8 TOPS + % roofline, B=128 H=12 N=197 d=64, 1 MI35
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's sources (the traffic record is tied to it)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_DIR)):
+    for name in sorted(n for n in os.listdir(KERNEL_DIR)
+                       if n.startswith("iqattn_") and n.endswith((".hip", ".h"))):
         h.update(name.encode())
         h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
     return h.hexdigest()[:16]

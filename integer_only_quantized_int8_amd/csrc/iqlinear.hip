@@ -5,16 +5,16 @@
 // Linear Operations" (integer product, then (b * acc) >> c to int8); sec. 3.1
 // (the MSA projections).
 //
-// Kernel: a workgroup of 2 x 2 waves computes a 128 (rows) x 128 (output
-// columns) tile as Y^T = W . X^T with v_mfma_i32_16x16x64_i8, so a lane ends
-// with 4 adjacent output columns of one row (one 4-byte store).  Each wave owns
-// 64 x 64: 4 x 4 MFMA tiles, 64 accumulator registers (larger wave tiles need
-// so many registers that one wave per SIMD remains, which measured slower).
-// The k loop steps by 64 bytes: the next step's X and W tiles (2 x 8 KB) are
-// loaded into registers while the current step runs from LDS, then written to
-// the other LDS buffer (double buffering, one barrier per step).  LDS rows are 64 bytes
-// with the 16-byte chunks XOR-swizzled by (row >> 1) & 3, which makes the
-// b128 operand reads of 16 rows x 4 chunks bank-conflict free.
+// Kernel (iqlinear_pipe below): persistent workgroups, one per CU, of 4 MFMA
+// waves and 4 loader waves.  Each workgroup computes 256 x 128 (or 128 x 128)
+// output tiles as Y^T = W . X^T with v_mfma_i32_16x16x64_i8, so a lane ends
+// with 4 adjacent output columns of one row (one 4-byte store after the fused
+// requantisation, straight into the head-split layout when asked).  Each
+// compute wave owns a quarter of the tile (128 x 64: 32 MFMA tiles, 128
+// accumulators).  The k loop steps by 64 bytes through a ring of LDS stages
+// filled by the loader waves with direct global->LDS loads; LDS rows are 64
+// bytes with the 16-byte chunks XOR-swizzled by (row >> 1) & 3, which makes
+// the b128 operand reads of 16 rows x 4 chunks bank-conflict free.
 #include "iqattn_dev.h"
 #include "iqattn.h"
 #include "iqlinear.h"
@@ -39,124 +39,239 @@ struct LinParams {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
 
-// Workgroup of WM x WN waves; each wave owns TM x TN MFMA tiles (16 x 16) of
-// rows x output columns, so the workgroup tile is (16 WM TM) x (16 WN TN).
-template <int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(64 * WM * WN) void iqlinear_gemm(LinParams p) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int BM = 16 * WM * TM, BN = 16 * WN * TN;   // workgroup tile
-  constexpr int XCH = BM * 4 / NT, WCH = BN * 4 / NT;   // 16-byte chunks per thread per step
-  static_assert(BM * 4 % NT == 0 && BN * 4 % NT == 0, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) int8_t sX[2][BM * kStep];
-  __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * kStep];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int li = lane & 15, g = lane >> 4;
-  const int wm = wave % WM, wn = wave / WM;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-
-  // global tile loads (rows past the end read as zeros: buffer range)
-  const __amdgpu_buffer_rsrc_t xr = buf_rsrc(p.x, (uint32_t)(p.rows * p.in_f));
-  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(p.w, (uint32_t)(p.out_f * p.in_f));
-  int xoff[XCH], xls[XCH], woff[WCH], wls[WCH];
-  bool xin[XCH];
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int idx = tid + NT * i, row = idx >> 2, ch = idx & 3;
-    xin[i] = m0 + row < p.rows;
-    xoff[i] = (xin[i] ? m0 + row : 0) * p.in_f + 16 * ch;
-    xls[i] = swz(row, ch);
-  }
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int idx = tid + NT * i, row = idx >> 2, ch = idx & 3;
-    woff[i] = (n0 + row) * p.in_f + 16 * ch;
-    wls[i] = swz(row, ch);
-  }
-  v4i xv[XCH], wv[WCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i] + k0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[i] + k0, 0, 0);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) *(v4i*)(sX[buf] + xls[i]) = xin[i] ? xv[i] : v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) *(v4i*)(sW[buf] + wls[i]) = wv[i];
-  };
-
-  v4i acc[TN][TM];  // [n tile][m tile]
-#pragma unroll
-  for (int a = 0; a < TN; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-
-  const int nks = p.in_f / kStep;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nks) gload((ks + 1) * kStep);
-    v4i bf[TM];
-#pragma unroll
-    for (int t = 0; t < TM; ++t) bf[t] = *(const v4i*)(sX[buf] + swz(16 * (TM * wm + t) + li, g));
-#pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const v4i af = *(const v4i*)(sW[buf] + swz(16 * (TN * wn + a) + li, g));  // output columns
-#pragma unroll
-      for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(af, bf[b], acc[a][b]);
-    }
-    if (ks + 1 < nks) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds output columns n0 + 16 (TN wn + a) + 4 g + r of row
-  // m0 + 16 (TM wm + b) + li
+// Epilogue of one wave's TN x TM accumulator tiles: acc[a][b][r] is output
+// column n + 16 a + r of row m + 16 b; requantised, packed to 4 bytes and
+// stored.  The destination offset splits into a row part and a column part
+// (plain: m out + n; head split: ((bidx H + h) N + t) d + i = (bidx H N + t) d
+// + (h N d + i)), so the divisions run once per row and once per column.
+// Rows past the end are skipped.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[TN][TM], int m_base,
+                                           int n_base) {
+  const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
+  int64_t rofs[TM];
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int m = m0 + 16 * (TM * wm + b) + li;
-    if (m >= p.rows) continue;
+    const int m = m_base + 16 * b;
+    if (qkv) {
+      const int bidx = m / p.seq_len, t = m - bidx * p.seq_len;
+      rofs[b] = ((int64_t)bidx * p.heads * p.seq_len + t) * p.head_dim;
+    } else {
+      rofs[b] = (int64_t)m * p.out_f;
+    }
+  }
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
-      const int n = n0 + 16 * (TN * wn + a) + 4 * g;
-      if (n >= p.out_f) continue;  // out is a multiple of 16: the whole 16-column tile
-      int which = 0, col = n;
-      if (p.layout == IQLINEAR_QKV_HEADS) {
-        which = n / p.width;
-        col = n - which * p.width;
-      }
-      int32_t y[4];
-      if (p.bm[which]) {
+  for (int a = 0; a < TN; ++a) {
+    const int n = n_base + 16 * a;
+    if (n >= p.out_f) continue;  // out is a multiple of 16: the whole 16-column tile
+    int which = 0, cofs = n;
+    if (qkv) {
+      which = n / p.width;
+      const int col = n - which * p.width;
+      const int h = col / p.head_dim;
+      cofs = h * p.seq_len * p.head_dim + (col - h * p.head_dim);
+    }
+    const int32_t bm = p.bm[which], bb = p.b[which], cc = p.c[which];
+    int8_t* const out = p.out[which];
+    if (bm) {  // uniform: the pair of this 16-column tile
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = clamp127(mulhi_i32(acc[a][b][r], p.bm[which]));
-      } else {
+      for (int b = 0; b < TM; ++b) {
+        if (m_base + 16 * b >= p.rows) continue;
+        *(uint32_t*)(out + rofs[b] + cofs) = pack4_lowbytes(
+            (uint32_t)clamp127(mulhi_i32(acc[a][b][0], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][1], bm)),
+            (uint32_t)clamp127(mulhi_i32(acc[a][b][2], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][3], bm)));
+      }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = requant_i8(acc[a][b][r], p.b[which], p.c[which]);
+      for (int b = 0; b < TM; ++b) {
+        if (m_base + 16 * b >= p.rows) continue;
+        *(uint32_t*)(out + rofs[b] + cofs) = pack4_lowbytes(
+            (uint32_t)requant_i8(acc[a][b][0], bb, cc), (uint32_t)requant_i8(acc[a][b][1], bb, cc),
+            (uint32_t)requant_i8(acc[a][b][2], bb, cc), (uint32_t)requant_i8(acc[a][b][3], bb, cc));
       }
-      const uint32_t word = pack4_lowbytes((uint32_t)y[0], (uint32_t)y[1], (uint32_t)y[2], (uint32_t)y[3]);
-      int64_t dst;
-      if (p.layout == IQLINEAR_QKV_HEADS) {
-        const int bidx = m / p.seq_len, t = m - bidx * p.seq_len;
-        const int h = col / p.head_dim, i = col - h * p.head_dim;
-        dst = (((int64_t)bidx * p.heads + h) * p.seq_len + t) * p.head_dim + i;
-      } else {
-        dst = (int64_t)m * p.out_f + n;
-      }
-      *(uint32_t*)(p.out[which] + dst) = word;
     }
   }
 }
 
-#ifndef IQLINEAR_CFG
-#define IQLINEAR_CFG 2, 2, 4, 4
-#endif
-constexpr int kCfg[4] = {IQLINEAR_CFG};
-#define IQLINEAR_KERNEL iqlinear_gemm<kCfg[0], kCfg[1], kCfg[2], kCfg[3]>
-constexpr int kBM = 16 * kCfg[0] * kCfg[2], kBN = 16 * kCfg[1] * kCfg[3];
-constexpr int kNT = 64 * kCfg[0] * kCfg[1];
+// ---------------------------------------------------------------- pipelined GEMM
+// Persistent workgroups (one per CU) of 4 compute waves and kPipeNL loader
+// waves.  The loaders stream the 64-byte k-slices of a tile's X rows and W rows
+// into a ring of kPipeNS LDS stages with direct global->LDS loads, each loader
+// wave a quarter of every stage (the swizzle is applied on the source side:
+// lane l of a 1 KB block fills LDS bytes [1024 i + 16 l, +16) = (row, chunk
+// position cp) from source chunk cp ^ ((row >> 1) & 3)), kPipeLag stages in
+// flight per wave, running ahead across tile boundaries.  Monotonic LDS
+// counters per stage slot: ready[b] (loader waves that finished a fill),
+// done[b] (compute waves that finished reading it).  Compute waves read the
+// fragments of the next stage while the MFMAs of the current one run.  Tiles
+// are dealt XCD-aware: the workgroups of one XCD (every 8th) take all column
+// tiles of one block of X rows in turn, so those rows reach that XCD's L2 once.
+constexpr int kPipeNS = 6;
+constexpr int kPipeLag = 4;
+constexpr int kPipeNL = 4;
+constexpr int kPipeSpin = 1 << 22;
+constexpr int kPipeThreads = 64 * (4 + kPipeNL);
+
+constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+template <int BM, int BN>
+struct PipeCfg {
+  static constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave (2 x 2 waves)
+  static constexpr int XB = BM * kStep, WB = BN * kStep, SB = XB + WB;
+  static constexpr int XI = XB / 1024 / kPipeNL, WI = WB / 1024 / kPipeNL;  // loads per loader wave
+  static constexpr int LDS = kPipeNS * SB + 64;
+};
+
+__device__ __forceinline__ void pipe_decode(int t, int ntn, int& tm, int& tn) {
+  const int x = t & 7, r = t >> 3, q = r / ntn;
+  tm = q * 8 + x;
+  tn = r - q * ntn;
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kPipeThreads) void iqlinear_pipe(LinParams p) {
+  typedef PipeCfg<BM, BN> C;
+  constexpr int TM = C::TM, TN = C::TN, NS = kPipeNS, NL = kPipeNL;
+  static_assert((C::XI + C::WI) * kPipeLag < 64, "vmcnt range");
+  static_assert(C::XI * NL * 1024 == C::XB && C::WI * NL * 1024 == C::WB, "stage split");
+  static_assert(kPipeLag < NS, "ring depth");
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  int* const ready = (int*)(smem + NS * C::SB);
+  int* const done = ready + NS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int G = (int)gridDim.x;
+  const int ntm = (p.rows + BM - 1) / BM, ntn = (p.out_f + BN - 1) / BN;
+  const int total_t = 8 * ntn * ((ntm + 7) / 8);
+  const int nks = p.in_f / kStep;
+  if (tid < NS) {
+    ready[tid] = 0;
+    done[tid] = 0;
+  }
+  __syncthreads();
+  const uint32_t sm0 = lds_addr(smem);
+
+  if (wave >= 4) {
+    // ---- loader wave wl: 1 KB blocks wl, wl + NL, ... of each stage's X and W parts
+    const int wl = wave - 4;
+    const v4i xr = make_rsrc(p.x, (uint32_t)(p.rows * p.in_f));
+    const v4i wr = make_rsrc(p.w, (uint32_t)(p.out_f * p.in_f));
+    auto mark = [&](int step) {
+      if (lane == 0)
+        __hip_atomic_fetch_add(&ready[step % NS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    int s = 0;
+    for (int t = blockIdx.x; t < total_t; t += G) {
+      int tm, tn;
+      pipe_decode(t, ntn, tm, tn);
+      if (tm >= ntm) continue;
+      const int m0 = tm * BM, n0 = tn * BN;
+      for (int ks = 0; ks < nks; ++ks, ++s) {
+        const int b = s % NS;
+        if (s >= NS) {  // the slot's previous step has been read by every compute wave
+          const int need = 4 * (s / NS);
+          int spins = 0;
+          while (__hip_atomic_load(&done[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+            if (++spins > kPipeSpin) return;
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        const uint32_t sb = sm0 + b * C::SB;
+#pragma unroll
+        for (int j = 0; j < C::XI; ++j) {
+          const int i = wl + NL * j;
+          const int o = 1024 * i + 16 * lane, row = o >> 6, cp = (o >> 4) & 3;
+          raw_buffer_load_lds(xr, (lds_u32w*)(uintptr_t)(sb + 1024 * i), 16,
+                              (m0 + row) * p.in_f + kStep * ks + 16 * (cp ^ ((row >> 1) & 3)), 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < C::WI; ++j) {
+          const int i = wl + NL * j;
+          const int o = 1024 * i + 16 * lane, row = o >> 6, cp = (o >> 4) & 3;
+          raw_buffer_load_lds(wr, (lds_u32w*)(uintptr_t)(sb + C::XB + 1024 * i), 16,
+                              (n0 + row) * p.in_f + kStep * ks + 16 * (cp ^ ((row >> 1) & 3)), 0, 0, 0);
+        }
+        // this wave's share of the stage issued kPipeLag steps ago has landed
+        if (s >= kPipeLag) {
+          __builtin_amdgcn_s_waitcnt(pipe_vmcnt(kPipeLag * (C::XI + C::WI)));
+          mark(s - kPipeLag);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(pipe_vmcnt(0));
+    for (int q = s - kPipeLag; q < s; ++q)
+      if (q >= 0) mark(q);
+    return;
+  }
+
+  // ---- compute waves: wave (wm, wn) owns rows 16 (TM wm + b) + li and columns
+  //      16 (TN wn + a) + 4 g + r of the tile
+  const int wm = wave & 1, wn = wave >> 1;
+  auto wait_ready = [&](int step) -> bool {
+    const int need = NL * (step / NS + 1);
+    int spins = 0;
+    while (__hip_atomic_load(&ready[step % NS], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+      if (++spins > kPipeSpin) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+  };
+  auto read_frags = [&](int step, v4i (&fx)[TM], v4i (&fw)[TN]) {
+    const int8_t* sb = smem + (step % NS) * C::SB;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) fx[b] = *(const v4i*)(sb + swz(16 * (TM * wm + b) + li, g));
+#pragma unroll
+    for (int a = 0; a < TN; ++a) fw[a] = *(const v4i*)(sb + C::XB + swz(16 * (TN * wn + a) + li, g));
+  };
+  auto signal_done = [&](int step) {
+    if (lane == 0) __hip_atomic_fetch_add(&done[step % NS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+
+  int s = 0;
+  for (int t = blockIdx.x; t < total_t; t += G) {
+    int tm, tn;
+    pipe_decode(t, ntn, tm, tn);
+    if (tm >= ntm) continue;
+    const int m0 = tm * BM, n0 = tn * BN;
+    v4i acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    // the fragments of step k are read while the MFMAs of step k - 1 run; a
+    // stage is released as soon as its fragments are in registers
+    v4i fx0[TM], fw0[TN], fx1[TM], fw1[TN];
+    if (!wait_ready(s)) return;
+    read_frags(s, fx0, fw0);
+    for (int ks = 0; ks < nks; ks += 2) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fx0, fw0 are in registers
+      signal_done(s + ks);
+      if (ks + 1 < nks) {
+        if (!wait_ready(s + ks + 1)) return;
+        read_frags(s + ks + 1, fx1, fw1);
+      }
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw0[a], fx0[b], acc[a][b]);
+      if (ks + 1 < nks) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // fx1, fw1 are in registers
+        signal_done(s + ks + 1);
+        if (ks + 2 < nks) {
+          if (!wait_ready(s + ks + 2)) return;
+          read_frags(s + ks + 2, fx0, fw0);
+        }
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw1[a], fx1[b], acc[a][b]);
+      }
+    }
+    s += nks;
+    store_tile<TM, TN>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
+  }
+}
 
 }  // namespace
 }  // namespace iqattn
@@ -166,6 +281,8 @@ using namespace iqattn;
 struct iqlinear_ctx {
   LinParams lp;
   int device;
+  int pipe_bm;    // 256 or 128: tile rows of the pipelined kernel
+  unsigned grid;  // persistent grid of the pipelined kernel
 };
 
 extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
@@ -218,6 +335,23 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
                       ((int64_t)p->b[k] << (32 - p->c[k])) < ((int64_t)1 << 31);
     lp.bm[i] = fast ? (int32_t)((int64_t)p->b[k] << (32 - p->c[k])) : 0;
   }
+  // pipelined kernel: one persistent workgroup per CU; 256-row tiles when each
+  // workgroup gets at least 4 of them, else 128-row tiles (finer at the end)
+  {
+    const int cus = prop.multiProcessorCount;
+    const int64_t ntn = (p->out_features + 127) / 128;
+    const int64_t t256 = ((int64_t)p->rows + 255) / 256 * ntn;
+    c->pipe_bm = t256 >= 4 * (int64_t)cus ? 256 : 128;
+    const int64_t tiles = ((int64_t)p->rows + c->pipe_bm - 1) / c->pipe_bm * ntn;
+    c->grid = (unsigned)(tiles < cus ? (tiles > 0 ? tiles : 1) : cus);
+    const void* k = c->pipe_bm == 256 ? (const void*)&iqlinear_pipe<256, 128>
+                                      : (const void*)&iqlinear_pipe<128, 128>;
+    const int lds = c->pipe_bm == 256 ? PipeCfg<256, 128>::LDS : PipeCfg<128, 128>::LDS;
+    if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+      free(c);
+      return IQATTN_E_DEVICE;
+    }
+  }
   *out = c;
   return IQATTN_OK;
 }
@@ -237,8 +371,13 @@ extern "C" int iqlinear_forward(iqlinear_ctx* c, const int8_t* x, const int8_t* 
   lp.out[0] = out0;
   lp.out[1] = qkv ? out1 : out0;
   lp.out[2] = qkv ? out2 : out0;
-  const dim3 grid((unsigned)((lp.rows + kBM - 1) / kBM), (unsigned)((lp.out_f + kBN - 1) / kBN));
-  hipLaunchKernelGGL(IQLINEAR_KERNEL, grid, dim3(kNT), 0, (hipStream_t)hip_stream, lp);
+  constexpr int lds256 = PipeCfg<256, 128>::LDS, lds128 = PipeCfg<128, 128>::LDS;
+  if (c->pipe_bm == 256)
+    hipLaunchKernelGGL((iqlinear_pipe<256, 128>), dim3(c->grid), dim3(kPipeThreads), lds256,
+                       (hipStream_t)hip_stream, lp);
+  else
+    hipLaunchKernelGGL((iqlinear_pipe<128, 128>), dim3(c->grid), dim3(kPipeThreads), lds128,
+                       (hipStream_t)hip_stream, lp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqlinear launch");
   return IQATTN_OK;
