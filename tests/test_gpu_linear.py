@@ -94,7 +94,8 @@ def test_linear_plain_shapes(torch_dev, rows, fin, fout):
     check(torch_dev, lw, label=f"plain {rows}x{fin}x{fout}")
 
 
-@pytest.mark.parametrize("B,N,H,d", [(1, 197, 3, 64), (2, 49, 3, 32), (3, 50, 2, 64), (1, 7, 1, 64)])
+@pytest.mark.parametrize("B,N,H,d", [(1, 197, 3, 64), (2, 49, 3, 32), (3, 50, 2, 64), (1, 7, 1, 64),
+                                     (2, 33, 4, 20), (1, 130, 4, 4)])
 def test_linear_qkv_head_split(torch_dev, B, N, H, d):
     lw = W.make_linear(B * N, 128, 3 * H * d, seed=B * 100 + N, qkv_heads=(B, N, H, d))
     check(torch_dev, lw, label=f"qkv B{B} N{N} H{H} d{d}")
