@@ -167,8 +167,8 @@ __device__ __forceinline__ void store_tile_lds(const LinParams& p, const v4i (&a
 // (every 8th) take all column tiles of one block of X rows in turn, so those
 // rows reach that XCD's L2 once.
 constexpr int kPipeKB = 128;  // k bytes of a row per stage: whole cache lines per request
-constexpr int kPipeNS = 3;
-constexpr int kPipeLag = 1;
+constexpr int kPipeNS = 4;
+constexpr int kPipeLag = 2;
 constexpr int kPipeNL = 4;
 constexpr int kPipeSpin = 1 << 22;
 constexpr int kPipeThreads = 64 * (4 + kPipeNL);
