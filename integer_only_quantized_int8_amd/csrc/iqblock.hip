@@ -58,7 +58,8 @@ struct LnDev {
   int32_t rows, cols;
   int32_t m, f;        // IntDiv exponent M, fraction bits F
   int32_t b, c;        // dyadic pair
-  int32_t bm, ywin;    // b << (32 - c) (RQ_MULHI); ceil(127 * 2^c / b) (RQ_WIN)
+  int32_t bm;          // b << (32 - c) (RQ_MULHI)
+  int32_t ylo, yhi;    // -floor(127 * 2^c / b), ceil(127 * 2^c / b) (RQ_WIN)
   uint32_t sqmask[6];  // bit k: ten Newton steps on k^2 - 1 end on k (not k - 1)
 };
 
@@ -99,17 +100,36 @@ __global__ void iqgelu_build_table(uint8_t* tab, int32_t i0, int32_t n, int32_t 
   tab[idx] = (uint8_t)(int8_t)res;
 }
 
+// Reductions over the G lanes of a row group, every lane receiving the result.
+// G = 16 (one DPP row): the pair and quad swaps (quad_perm [1,0,3,2] and
+// [2,3,0,1]), then row_half_mirror and row_mirror, which pair each lane with
+// one in the other quad and the other half-row -- VALU operations only.
+// G = 64: lane-index shuffles.
 template <int G>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  if constexpr (G == 16) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  } else {
 #pragma unroll
-  for (int s = 1; s < G; s <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, s, 64));
+    for (int s = 1; s < G; s <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, s, 64));
+  }
   return v;
 }
 
 template <int G>
 __device__ __forceinline__ int32_t group_sum_i32(int32_t v) {
+  if constexpr (G == 16) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);
+  } else {
 #pragma unroll
-  for (int s = 1; s < G; s <<= 1) v += __shfl_xor(v, s, 64);
+    for (int s = 1; s < G; s <<= 1) v += __shfl_xor(v, s, 64);
+  }
   return v;
 }
 
@@ -259,9 +279,11 @@ __device__ __forceinline__ int32_t med3_i32(int32_t x, int32_t lo, int32_t hi) {
 //   RQ_WIDE: 64-bit (b * y) >> c;
 //   RQ_MULHI: int32 y saturated, mulhi(y, b << (32 - c)) (when b << (32 - c) <
 //     2^31 and a saturated y clips either way);
-//   RQ_WIN: y saturated, then clamped to +-ywin = ceil(127 * 2^c / b) (beyond
-//     it the clipped result is +-127 already), then a 24-bit multiply by b and a
-//     shift (when b, ywin < 2^23 and 127 * 2^c + b < 2^31 keep it exact).
+//   RQ_WIN: y saturated, then clamped to [ylo, yhi] = [-floor(127 * 2^c / b),
+//     ceil(127 * 2^c / b)], then a 24-bit multiply by b and a shift.  With
+//     b <= 2^c the clamped bounds give exactly -127 and 127 and every y beyond
+//     them clips to those values, so no further clip is needed; b, yhi < 2^23
+//     and 127 * 2^c + b < 2^31 keep the product exact.
 constexpr int RQ_WIDE = 0, RQ_MULHI = 1, RQ_WIN = 2;
 
 // gamma and beta sit in LDS, one copy per block, laid out chunk-major: entry
@@ -313,7 +335,7 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
   __syncthreads();
   const float rcols = __builtin_amdgcn_rcpf((float)p.cols);
   const int32_t sh = p.m - p.f;
-  const int32_t nywin = -p.ywin;
+  const int32_t ylo = p.ylo;
 
   for (; r0 < p.rows; r0 += step) {
     const int row = r0 + wave * RPW + sub;
@@ -362,8 +384,8 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
           int32_t y;
           if constexpr (RQ == RQ_WIN) {
             const int32_t ys = mad24_sat(nrm, gv, bv);
-            const int32_t yc = med3_i32(ys, nywin, p.ywin);
-            y = clamp127(__mul24(yc, p.b) >> p.c);
+            const int32_t yc = med3_i32(ys, ylo, p.yhi);
+            y = __mul24(yc, p.b) >> p.c;  // in [-127, 127] by the choice of bounds
           } else if constexpr (RQ == RQ_MULHI) {
             const int32_t ys = mad24_sat(nrm, gv, bv);
             y = clamp127(__mulhi(ys, p.bm));
@@ -542,16 +564,19 @@ extern "C" int iqlayernorm_create(const iqlayernorm_params* p, iqlayernorm_ctx**
     return IQATTN_E_INVAL;
   int dev = 0;
   if ((rc = check_device(&dev))) return rc;
-  // The requantisation form: RQ_WIN when b, ywin < 2^23 and 127 * 2^c + b <
-  // 2^31; else RQ_MULHI when b << (32 - c) < 2^31 and (2^31 - 1) b / 2^c >= 128
-  // (a saturated y clips either way); else the 64-bit form.
+  // The requantisation form: RQ_WIN when b <= 2^c, b, yhi < 2^23 and
+  // 127 * 2^c + b < 2^31; else RQ_MULHI when b << (32 - c) < 2^31 and
+  // (2^31 - 1) b / 2^c >= 128 (a saturated y clips either way); else the
+  // 64-bit form.
   int rq = RQ_WIDE;
-  int32_t bm = 0, ywin = 0;
-  if (p->c <= 31) {
-    const int64_t yw = (((int64_t)127 << p->c) + p->b - 1) / p->b;
-    if (p->b < (1 << 23) && yw < (1 << 23) && ((int64_t)127 << p->c) + p->b < ((int64_t)1 << 31)) {
+  int32_t bm = 0, ylo = 0, yhi = 0;
+  if (p->c <= 31 && (int64_t)p->b <= ((int64_t)1 << p->c)) {
+    const int64_t a = (int64_t)127 << p->c;
+    const int64_t hi = (a + p->b - 1) / p->b, lo = -(a / p->b);
+    if (p->b < (1 << 23) && hi < (1 << 23) && a + p->b < ((int64_t)1 << 31)) {
       rq = RQ_WIN;
-      ywin = (int32_t)yw;
+      ylo = (int32_t)lo;
+      yhi = (int32_t)hi;
     }
   }
   if (rq == RQ_WIDE && p->c >= 1 && p->c <= 32) {
@@ -588,7 +613,8 @@ extern "C" int iqlayernorm_create(const iqlayernorm_params* p, iqlayernorm_ctx**
   d.b = p->b;
   d.c = p->c;
   d.bm = bm;
-  d.ywin = ywin;
+  d.ylo = ylo;
+  d.yhi = yhi;
   {
     uint8_t* flags = NULL;
     uint8_t host[192];
