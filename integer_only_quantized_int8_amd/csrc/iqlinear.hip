@@ -38,59 +38,100 @@ struct LinParams {
   int32_t layout;
   int32_t seq_len, heads, head_dim, width;  // width = heads * head_dim (QKV)
   int32_t b[3], c[3], bm[3];  // bm = b << (32 - c) when it is below 2^31, else 0
+  // Window path (w24 = 1 when every pair in use qualifies): for b <= 2^c the
+  // saturated result equals floor(b y / 2^c) of y = acc clamped to
+  // [ylo, yhi] = [ceil(-127 2^c / b), floor((128 2^c - 1) / b)] (floor(b y /
+  // 2^c) moves by at most 1 per unit of y, so it is -127 at ylo and 127 at
+  // yhi); when the window and bm24 = b 2^(32 - c) fit in 24 signed bits that
+  // is one v_mul_hi_i32_i24 of the clamped y and bm24.
+  int32_t ylo[3], yhi[3], bm24[3];
+  int32_t w24;
+  // floor(m / seq_len) = (m + mulhi(seq_magic, m)) >> seq_shift for 0 <= m < 2^31
+  // (Granlund and Montgomery's division by an invariant integer)
+  uint32_t seq_magic;
+  int32_t seq_shift;
 };
 
+template <typename T>
+__device__ __forceinline__ T pick3(int which, T a0, T a1, T a2) {
+  return which == 0 ? a0 : (which == 1 ? a1 : a2);
+}
+
+// floor(x * m / 2^32) for x, m in the signed 24-bit range: v_mul_hi_i32_i24
+__device__ __forceinline__ int32_t mulhi_i24(int32_t x, int32_t m) {
+  const int64_t xs = (int32_t)((uint32_t)x << 8) >> 8, ms = (int32_t)((uint32_t)m << 8) >> 8;
+  return (int32_t)((xs * ms) >> 32);
+}
+
+__device__ __forceinline__ int32_t div_seq(const LinParams& p, int32_t m) {
+  return (int32_t)(((uint32_t)m + mulhi_u32(p.seq_magic, (uint32_t)m)) >> p.seq_shift);
+}
+
+// The four requantised bytes of accumulator block v (4 adjacent columns of
+// one row, all under the pair `which`), packed little-endian.
+template <bool W24>
+__device__ __forceinline__ uint32_t requant4(const LinParams& p, int which, v4i v) {
+  if (W24) {
+    const int32_t lo = pick3(which, p.ylo[0], p.ylo[1], p.ylo[2]);
+    const int32_t hi = pick3(which, p.yhi[0], p.yhi[1], p.yhi[2]);
+    const int32_t m = pick3(which, p.bm24[0], p.bm24[1], p.bm24[2]);
+    uint32_t r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      r[k] = (uint32_t)mulhi_i24(__builtin_elementwise_max(__builtin_elementwise_min(v[k], hi), lo), m);
+    return pack4_lowbytes(r[0], r[1], r[2], r[3]);
+  }
+  const int32_t bm = pick3(which, p.bm[0], p.bm[1], p.bm[2]);
+  if (bm)
+    return pack4_lowbytes((uint32_t)clamp127(mulhi_i32(v[0], bm)), (uint32_t)clamp127(mulhi_i32(v[1], bm)),
+                          (uint32_t)clamp127(mulhi_i32(v[2], bm)), (uint32_t)clamp127(mulhi_i32(v[3], bm)));
+  const int32_t bb = pick3(which, p.b[0], p.b[1], p.b[2]), cc = pick3(which, p.c[0], p.c[1], p.c[2]);
+  return pack4_lowbytes((uint32_t)requant_i8(v[0], bb, cc), (uint32_t)requant_i8(v[1], bb, cc),
+                        (uint32_t)requant_i8(v[2], bb, cc), (uint32_t)requant_i8(v[3], bb, cc));
+}
+
+// Destination of output row m (its part of the offset): plain m out; head
+// split (bidx H N + t) d = m d + bidx (H - 1) N d for m = bidx N + t.
+__device__ __forceinline__ int64_t row_offset(const LinParams& p, bool qkv, int m) {
+  if (!qkv) return (int64_t)m * p.out_f;
+  const int bidx = div_seq(p, m);
+  return (int64_t)m * p.head_dim + (int64_t)bidx * (p.heads - 1) * p.seq_len * p.head_dim;
+}
+
+// Column part of the destination of output column n (a multiple of 4) and the
+// tensor it belongs to: plain n; head split (h N d + i) for column n = which
+// width + h d + i.  n / head_dim runs once per lane and tile.
+__device__ __forceinline__ int col_part(const LinParams& p, bool qkv, int n, int& which) {
+  if (!qkv) {
+    which = 0;
+    return n;
+  }
+  which = (n >= p.width) + (n >= 2 * p.width);
+  const int col = n - which * p.width, h = col / p.head_dim;
+  return h * p.seq_len * p.head_dim + (col - h * p.head_dim);
+}
 
 // Epilogue of one wave's TN x TM accumulator tiles: acc[a][b][r] is output
 // column n + 16 a + r of row m + 16 b; requantised, packed to 4 bytes and
-// stored.  The destination offset splits into a row part and a column part
-// (plain: m out + n; head split: ((bidx H + h) N + t) d + i = (bidx H N + t) d
-// + (h N d + i)), so the divisions run once per row and once per column.
-// Rows past the end are skipped.
-template <int TM, int TN>
+// stored.  Rows past the end are skipped.
+template <int TM, int TN, bool W24>
 __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[TN][TM], int m_base,
                                            int n_base) {
   const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
   int64_t rofs[TM];
 #pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int m = m_base + 16 * b;
-    if (qkv) {
-      const int bidx = m / p.seq_len, t = m - bidx * p.seq_len;
-      rofs[b] = ((int64_t)bidx * p.heads * p.seq_len + t) * p.head_dim;
-    } else {
-      rofs[b] = (int64_t)m * p.out_f;
-    }
-  }
+  for (int b = 0; b < TM; ++b) rofs[b] = row_offset(p, qkv, m_base + 16 * b);
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     const int n = n_base + 16 * a;
     if (n >= p.out_f) continue;  // out is a multiple of 16: the whole 16-column tile
-    int which = 0, cofs = n;
-    if (qkv) {
-      which = n / p.width;
-      const int col = n - which * p.width;
-      const int h = col / p.head_dim;
-      cofs = h * p.seq_len * p.head_dim + (col - h * p.head_dim);
-    }
-    const int32_t bm = p.bm[which], bb = p.b[which], cc = p.c[which];
-    int8_t* const out = p.out[which];
-    if (bm) {  // uniform: the pair of this 16-column tile
+    int which;
+    const int cofs = col_part(p, qkv, n, which);
+    int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]);
 #pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        if (m_base + 16 * b >= p.rows) continue;
-        *(uint32_t*)(out + rofs[b] + cofs) = pack4_lowbytes(
-            (uint32_t)clamp127(mulhi_i32(acc[a][b][0], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][1], bm)),
-            (uint32_t)clamp127(mulhi_i32(acc[a][b][2], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][3], bm)));
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < TM; ++b) {
-        if (m_base + 16 * b >= p.rows) continue;
-        *(uint32_t*)(out + rofs[b] + cofs) = pack4_lowbytes(
-            (uint32_t)requant_i8(acc[a][b][0], bb, cc), (uint32_t)requant_i8(acc[a][b][1], bb, cc),
-            (uint32_t)requant_i8(acc[a][b][2], bb, cc), (uint32_t)requant_i8(acc[a][b][3], bb, cc));
-      }
+    for (int b = 0; b < TM; ++b) {
+      if (m_base + 16 * b >= p.rows) continue;
+      *(uint32_t*)(out + rofs[b] + cofs) = requant4<W24>(p, which, acc[a][b]);
     }
   }
 }
@@ -101,54 +142,38 @@ __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[
 // stores whole 16-byte row chunks (4 x fewer store instructions, contiguous
 // 16-byte writes).  Needs 16-column groups that stay inside one output row
 // segment: always for the plain layout, head_dim % 16 == 0 for the head split.
+// The pair of a 16-column group is wave-uniform (n_w is), so it is picked from
+// scalar registers; the output tensor of a lane's chunk is picked by selects.
 constexpr int kEpPitch = 16 * 4 + 16;  // (16 TN = 64) bytes + 16 of padding
 
-template <int TM, int TN>
+template <int TM, int TN, bool W24>
 __device__ __forceinline__ void store_tile_lds(const LinParams& p, const v4i (&acc)[TN][TM],
                                                int8_t* scr, int m_w, int n_w, int li, int g,
                                                int lane) {
   static_assert(16 * TN + 16 == kEpPitch, "pitch");
+  static_assert(64 % TN == 0, "a lane's chunks share one column group");
   const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
     const int n = n_w + 16 * a;
-    const int which = qkv ? n / p.width : 0;
-    const int32_t bm = p.bm[which], bb = p.b[which], cc = p.c[which];
+    const int which = qkv ? (n >= p.width) + (n >= 2 * p.width) : 0;
 #pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      uint32_t word;
-      if (bm)
-        word = pack4_lowbytes(
-            (uint32_t)clamp127(mulhi_i32(acc[a][b][0], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][1], bm)),
-            (uint32_t)clamp127(mulhi_i32(acc[a][b][2], bm)), (uint32_t)clamp127(mulhi_i32(acc[a][b][3], bm)));
-      else
-        word = pack4_lowbytes(
-            (uint32_t)requant_i8(acc[a][b][0], bb, cc), (uint32_t)requant_i8(acc[a][b][1], bb, cc),
-            (uint32_t)requant_i8(acc[a][b][2], bb, cc), (uint32_t)requant_i8(acc[a][b][3], bb, cc));
-      *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = word;
-    }
+    for (int b = 0; b < TM; ++b)
+      *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = requant4<W24>(p, which, acc[a][b]);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS (one wave: in order)
-  constexpr int CH = TM * TN;          // 16-byte chunks per lane: (16 TM rows x TN chunks) / 16 ... / 64 lanes x 16
+  // lane chunk k: row lane / TN + (64 / TN) k of the block, column group lane % TN
+  const int cg = lane % TN, n = n_w + 16 * cg;
+  int which;
+  const int cofs = col_part(p, qkv, n, which);
+  int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]) + cofs;
+  const bool col_ok = n < p.out_f;
 #pragma unroll
   for (int k = 0; k < (16 * TM * TN) / 64; ++k) {
-    const int c = lane + 64 * k, row = c / TN, cg = c % TN;
-    const int m = m_w + row, n = n_w + 16 * cg;
+    const int row = lane / TN + (64 / TN) * k, m = m_w + row;
     const v4i v = *(const v4i*)(scr + row * kEpPitch + 16 * cg);
-    if (m >= p.rows || n >= p.out_f) continue;
-    int64_t dst;
-    int which = 0;
-    if (qkv) {
-      which = n / p.width;
-      const int col = n - which * p.width, h = col / p.head_dim;
-      const int bidx = m / p.seq_len, t = m - bidx * p.seq_len;
-      dst = (((int64_t)bidx * p.heads + h) * p.seq_len + t) * p.head_dim + (col - h * p.head_dim);
-    } else {
-      dst = (int64_t)m * p.out_f + n;
-    }
-    *(v4i*)(p.out[which] + dst) = v;
+    if (m < p.rows && col_ok) *(v4i*)(out + row_offset(p, qkv, m)) = v;
   }
-  (void)CH;
   __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the block is reused
 }
 
@@ -312,35 +337,54 @@ __global__ __launch_bounds__(kPipeThreads) void iqlinear_pipe(LinParams p) {
       for (int b = 0; b < TM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
     // per stage: block 1's fragments are read while block 0's MFMAs run, the
     // stage is released once they are in registers, and the next stage's
-    // block 0 is read while block 1's MFMAs run
+    // block 0 is read while block 1's MFMAs run.  The MFMAs of the loop body
+    // are unconditional (a conditional accumulator update makes the compiler
+    // copy every accumulator register each iteration); an odd k-block count
+    // ends with a one-block stage after the loop.
     v4i fx0[TM], fw0[TN], fx1[TM], fw1[TN];
     if (!wait_ready(s)) return;
     read_frags(s, J0(), fx0, fw0);
-    for (int st = 0; st < nks; ++st) {
-      const bool two = 2 * st + 1 < nkb;  // the stage's second k-block exists
-      if (two) read_frags(s + st, J1(), fx1, fw1);
+    const int nfull = nkb >> 1;  // stages holding two k-blocks
+    for (int st = 0; st < nfull; ++st) {
+      read_frags(s + st, J1(), fx1, fw1);
 #pragma unroll
       for (int a = 0; a < TN; ++a)
 #pragma unroll
         for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw0[a], fx0[b], acc[a][b]);
+      // the MFMAs are issued before the wait (the scheduler would otherwise
+      // hoist the wait above them and expose the fragment reads' latency)
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every fragment of the stage is in registers
       signal_done(s + st);
       if (st + 1 < nks) {
         if (!wait_ready(s + st + 1)) return;
         read_frags(s + st + 1, J0(), fx0, fw0);
       }
-      if (two) {
 #pragma unroll
-        for (int a = 0; a < TN; ++a)
+      for (int a = 0; a < TN; ++a)
 #pragma unroll
-          for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw1[a], fx1[b], acc[a][b]);
-      }
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw1[a], fx1[b], acc[a][b]);
+    }
+    if (nkb & 1) {  // the last stage's single k-block is in fx0, fw0
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw0[a], fx0[b], acc[a][b]);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      signal_done(s + nfull);
     }
     s += nks;
-    if (wide_ep)
-      store_tile_lds<TM, TN>(p, acc, ep_scr, m0 + 16 * TM * wm, n0 + 16 * TN * wn, li, g, lane);
-    else
-      store_tile<TM, TN>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
+    if (wide_ep) {
+      if (p.w24)
+        store_tile_lds<TM, TN, true>(p, acc, ep_scr, m0 + 16 * TM * wm, n0 + 16 * TN * wn, li, g, lane);
+      else
+        store_tile_lds<TM, TN, false>(p, acc, ep_scr, m0 + 16 * TM * wm, n0 + 16 * TN * wn, li, g, lane);
+    } else {
+      if (p.w24)
+        store_tile<TM, TN, true>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
+      else
+        store_tile<TM, TN, false>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
+    }
   }
 }
 
@@ -397,15 +441,41 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
   lp.heads = p->heads;
   lp.head_dim = p->head_dim;
   lp.width = p->heads * p->head_dim;
+  lp.w24 = 1;
   for (int i = 0; i < 3; ++i) {
     const int k = i < npairs ? i : 0;
-    lp.b[i] = p->b[k];
-    lp.c[i] = p->c[k];
-    const bool fast = p->c[k] >= 1 && p->c[k] <= 32 &&
-                      ((int64_t)p->b[k] << (32 - p->c[k])) < ((int64_t)1 << 31);
-    lp.bm[i] = fast ? (int32_t)((int64_t)p->b[k] << (32 - p->c[k])) : 0;
+    const int64_t b = p->b[k];
+    const int c = p->c[k];
+    lp.b[i] = (int32_t)b;
+    lp.c[i] = c;
+    const bool fast = c >= 1 && c <= 32 && (b << (32 - c)) < ((int64_t)1 << 31);
+    lp.bm[i] = fast ? (int32_t)(b << (32 - c)) : 0;
+    // window path: bm24 = b 2^(32 - c) < 2^23 (so b <= 2^c) and the window
+    // [ceil(-127 2^c / b), floor((128 2^c - 1) / b)] inside [-2^23, 2^23 - 1]
+    bool w = c <= 32 && (b << (32 - c)) < ((int64_t)1 << 23);
+    if (w) {
+      const int64_t lo = -((127 * ((int64_t)1 << c)) / b);
+      const int64_t hi = (128 * ((int64_t)1 << c) - 1) / b;
+      w = lo >= -((int64_t)1 << 23) && hi <= ((int64_t)1 << 23) - 1;
+      lp.ylo[i] = w ? (int32_t)lo : 0;
+      lp.yhi[i] = w ? (int32_t)hi : 0;
+      lp.bm24[i] = w ? (int32_t)(b << (32 - c)) : 0;
+    }
+    if (!w) lp.w24 = 0;
   }
-  // pipelined kernel: one persistent workgroup per CU, 128 x 128 tiles
+  // floor(m / seq_len) for the head split: l = ceil(log2 seq_len), magic =
+  // floor(2^32 (2^l - seq_len) / seq_len) + 1 (below 2^32 since 2^l - seq_len
+  // < seq_len); exact for 0 <= m < 2^31
+  lp.seq_magic = 0;
+  lp.seq_shift = 0;
+  if (p->layout == IQLINEAR_QKV_HEADS) {
+    const uint64_t d = (uint64_t)p->seq_len;
+    int l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    lp.seq_magic = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
+    lp.seq_shift = l;
+  }
+  // persistent kernels: one workgroup per CU, 128 x 128 tiles
   {
     const int cus = prop.multiProcessorCount;
     const int64_t tiles = ((int64_t)p->rows + 127) / 128 * ((p->out_features + 127) / 128);

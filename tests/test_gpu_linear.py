@@ -101,11 +101,67 @@ def test_linear_qkv_head_split(torch_dev, B, N, H, d):
     check(torch_dev, lw, label=f"qkv B{B} N{N} H{H} d{d}")
 
 
+@pytest.mark.parametrize("rows,fin,fout", [
+    (4229, 512, 1152), (8200, 768, 640), (16387, 256, 2048),
+])
+def test_linear_several_tiles_per_workgroup(torch_dev, rows, fin, fout):
+    """More 128 x 128 tiles than compute units, so that each persistent
+    workgroup walks a run of tiles and meets a new 128-row block of X inside
+    its run; every element against the oracle."""
+    lw = W.make_linear(rows, fin, fout, seed=rows ^ fin ^ fout)
+    check(torch_dev, lw, label=f"multi-tile {rows}x{fin}x{fout}")
+
+
+def test_linear_qkv_head_split_several_tiles(torch_dev):
+    B, N, H, d = 32, 197, 4, 64
+    lw = W.make_linear(B * N, 768, 3 * H * d, seed=77, qkv_heads=(B, N, H, d))
+    check(torch_dev, lw, label=f"qkv multi-tile B{B} N{N} H{H} d{d}")
+
+
 def test_linear_extreme_dyadic_pairs(torch_dev):
     lw = W.make_linear(70, 128, 64, seed=3, sigma_x=127.0, sigma_w=127.0)
     for b, c in ((1, 0), ((1 << 31) - 1, 62), ((1 << 31) - 1, 40), ((1 << 15) - 1, 32),
                  (1 << 14, 1), (3, 12)):
         check(torch_dev, lw, params=dict(lw.params, b=(b,), c=(c,)), label=f"b={b} c={c}")
+
+
+def _extreme_operands(rows, fin, fout, seed):
+    """x and w whose products reach the int32 accumulator's extremes for this
+    depth (+-fin 127 128 and +-fin 127 127) in some rows and columns, random
+    Gaussians elsewhere."""
+    lw = W.make_linear(rows, fin, fout, seed=seed, sigma_x=60.0, sigma_w=60.0)
+    x, w = lw.x.copy(), lw.w.copy()
+    x[0], x[1], x[2] = 127, -128, -127
+    x[3, ::2], x[3, 1::2] = 127, -128
+    w[0], w[1], w[2] = 127, -128, -127
+    w[5, ::2], w[5, 1::2] = -128, 127
+    lw.x, lw.w = x, w
+    return lw
+
+
+@pytest.mark.parametrize("b,c", [
+    (65536, 32),        # the window reaches 2^23 - 1 exactly: the 24-bit path
+    (65535, 32),        # one step outside: the general path
+    ((1 << 23) - 1, 32), (2047, 20), (1 << 22, 31), (3, 12), (1, 10), (5, 16),
+])
+def test_linear_requant_window_edges(torch_dev, b, c):
+    """Pairs on both sides of the 24-bit window path's limits, with
+    accumulators at the int32 extremes of a 1024-deep product so that both
+    ends of the window saturate."""
+    lw = _extreme_operands(140, 1024, 96, seed=b % 1000 + c)
+    check(torch_dev, lw, params=dict(lw.params, b=(b,), c=(c,)), label=f"window b={b} c={c}")
+
+
+def test_linear_qkv_mixed_pair_paths(torch_dev):
+    """Head split with one pair outside the window path (the whole launch
+    takes the general path) and with three different window pairs."""
+    B, N, H, d = 2, 70, 4, 32
+    base = W.make_linear(B * N, 256, 3 * H * d, seed=91, sigma_x=60.0, sigma_w=60.0,
+                         qkv_heads=(B, N, H, d))
+    for pairs in (((1 << 14) + 3, 24), (5000, 20), ((1 << 31) - 1, 45)), \
+                 (((1 << 14) + 3, 24), (2000, 22), (3, 12)):
+        P = dict(base.params, b=tuple(p[0] for p in pairs), c=tuple(p[1] for p in pairs))
+        check(torch_dev, base, params=P, label=f"qkv pairs {pairs}")
 
 
 def test_linear_vitb_projections_sampled_rows(torch_dev):
