@@ -147,6 +147,21 @@ def bench_linear(args):
                         "unit": "TFLOP/s", "frac": round(ktops / MFMA_I8_PEAK_TOPS, 4),
                         "traffic": None, "algorithmic_bytes_per_launch": int(hbm),
                         "hbm_gbs_at_algorithmic_bytes": round(hbm / (kern_ms * 1e-3) / 1e9, 1)}}
+    if not args.no_cpu:
+        # the oracle on the first rows of the same x (every output column, each
+        # (b, c) pair on its slice of W), a bounded sample of about 2 s
+        import oracle
+        rows = min(M, 1536)
+        npairs = 3 if P["layout"] == 1 else 1
+        width = Nc // npairs
+        t1 = time.perf_counter()
+        for i in range(npairs):
+            oracle.linear(lw.x[:rows], lw.w[i * width:(i + 1) * width], P["b"][i], P["c"][i])
+        cpu_s = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": round(2.0 * rows * K * Nc / cpu_s / 1e12, 6),
+                               "unit": "TOPS", "cores": 1, "kind": "oracle",
+                               "sample": f"the first {rows} of {M} rows, all {Nc} output columns, "
+                                         f"{cpu_s:.2f} s single-threaded C -O2 on {cpu_model()}"}
     lin.close()
     print(json.dumps(res), flush=True)
 
