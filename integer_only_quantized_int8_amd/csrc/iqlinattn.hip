@@ -10,8 +10,8 @@
 // or written once (4 N d bytes per head), so the kernel is HBM-bound and both
 // contractions run on int8 MFMA (v_mfma_i32_16x16x32_i8):
 //   phase 1 (steps i, ii): each wave streams 32-token chunks of K and V
-//     through its own LDS slot (two chunks in flight in registers, the first
-//     issued at kernel entry); ds_read_b64_tr_b8 turns the row-major chunk
+//     through its own LDS slot (four chunks in flight in registers, the
+//     first issued at kernel entry); ds_read_b64_tr_b8 turns the row-major chunk
 //     into the token-major MFMA operands, so that one MFMA per 16 x 16 tile of
 //     KV = ReLU(K)^T V sums 32 tokens; ks = sum ReLU(K) comes from v_dot4 on
 //     the same operand bytes.  ReLU acts on the operand bytes (a byte mask).
@@ -41,7 +41,7 @@ namespace {
 constexpr int kLaWaves = IQLA_WAVES;
 constexpr int kLaThreads = 64 * kLaWaves;
 constexpr int kChunk = 32;       // tokens per MFMA step of the token sums
-constexpr int kKVDepth = 2;      // K/V chunks in flight per wave (phase 1)
+constexpr int kKVDepth = 4;      // K/V chunks in flight per wave (phase 1)
 constexpr int kQDepth = 4;       // 16-token Q tiles in flight per wave (phase 2)
 
 struct LaParams {
