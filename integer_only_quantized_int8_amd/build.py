@@ -32,9 +32,14 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+BUILD_DIR = os.path.join(ROOT, "_build")  # in-tree scratch for objects (not tracked)
+
+
 def build(verbose: bool = False) -> str:
     srcs = sources()
-    with tempfile.TemporaryDirectory(prefix="iqattn_build_") as tmpd:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    env = dict(os.environ, TMPDIR=BUILD_DIR)  # the compiler's own temporaries too
+    with tempfile.TemporaryDirectory(prefix="iqattn_build_", dir=BUILD_DIR) as tmpd:
         objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in srcs]
 
         def compile_one(args):
@@ -43,7 +48,7 @@ def build(verbose: bool = False) -> str:
             cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            subprocess.check_call(cmd)
+            subprocess.check_call(cmd, env=env)
 
         with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
             list(ex.map(compile_one, zip(srcs, objs)))
@@ -51,7 +56,7 @@ def build(verbose: bool = False) -> str:
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        subprocess.check_call(cmd, env=env)
         os.replace(tmp, LIB)
     return LIB
 

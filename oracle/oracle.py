@@ -25,8 +25,11 @@ def build(force: bool = True) -> str:
     """Compile the oracle (single-threaded, -O2, C99)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
+        # the compiler's temporaries go to the repository's untracked _build/
+        scratch = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(_SRC))), "_build")
+        os.makedirs(scratch, exist_ok=True)
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC",
-                               "-shared", "-o", tmp, _SRC])
+                               "-shared", "-o", tmp, _SRC], env=dict(os.environ, TMPDIR=scratch))
         os.replace(tmp, _LIB)
     return _LIB
 
