@@ -164,6 +164,20 @@ def test_linear_qkv_mixed_pair_paths(torch_dev):
         check(torch_dev, base, params=P, label=f"qkv pairs {pairs}")
 
 
+@pytest.mark.parametrize("B,N,H,d", [(2, 33, 4, 20), (1, 130, 4, 4)])
+def test_linear_qkv_narrow_heads_general_pairs(torch_dev, B, N, H, d):
+    """Head dims that are not a multiple of 16 (per-lane 4-byte stores) with
+    pairs outside the 24-bit window path: the 32-bit multiply-high form, the
+    64-bit form, and a mix of both over Q, K and V."""
+    lw = W.make_linear(B * N, 128, 3 * H * d, seed=B * 31 + N, sigma_x=80.0, sigma_w=80.0,
+                       qkv_heads=(B, N, H, d))
+    for pairs in (((1 << 31) - 1, 45), (((1 << 31) - 1, 40), ((1 << 31) - 1, 40), (5000, 20))):
+        if isinstance(pairs[0], int):
+            pairs = (pairs, pairs, pairs)
+        P = dict(lw.params, b=tuple(x[0] for x in pairs), c=tuple(x[1] for x in pairs))
+        check(torch_dev, lw, params=P, label=f"qkv narrow B{B} N{N} H{H} d{d} pairs {pairs}")
+
+
 def test_linear_vitb_projections_sampled_rows(torch_dev):
     for name in W.LINEAR_CONFIGS:
         lw = W.linear_workload(name)
