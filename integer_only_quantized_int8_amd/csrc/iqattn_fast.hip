@@ -146,15 +146,25 @@ __device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t v
 // s_waitcnt immediate for vmcnt(n), other counters untouched (n < 64)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// V^T operands of one 64-key step (FT 16-feature tiles) by transpose reads:
-// two ds_read_b64_tr_b8 per tile at the lane offsets vtr[0], vtr[1], the
-// feature tile entering as an XOR of the 16-byte chunk index.
-template <int D, int FT>
-__device__ __forceinline__ void read_vt(uint32_t vb, const int (&vtr)[2], v4i (&vop)[FT]) {
+// V^T operands by transpose reads: two ds_read_b64_tr_b8 per 16-feature tile
+// at the lane offsets vtr[0], vtr[1], the feature tile entering as an XOR of
+// the 16-byte chunk index.  vt_addr forms a tile's eight lane addresses once;
+// read_vt adds the 64-key step's byte offset, a constant the reads carry in
+// their offset field.
+template <int FT>
+__device__ __forceinline__ void vt_addr(uint32_t vb, const int (&vtr)[2], uint32_t (&va)[FT][2]) {
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(vb + (vtr[0] ^ (ft << 4))));
-    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(vb + (vtr[1] ^ (ft << 4))));
+    va[ft][0] = vb + (uint32_t)(vtr[0] ^ (ft << 4));
+    va[ft][1] = vb + (uint32_t)(vtr[1] ^ (ft << 4));
+  }
+}
+template <int FT>
+__device__ __forceinline__ void read_vt(const uint32_t (&va)[FT][2], uint32_t off, v4i (&vop)[FT]) {
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][0] + off));
+    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][1] + off));
     vop[ft] = v4i{r0[0], r0[1], r1[0], r1[1]};
   }
 }
@@ -366,11 +376,16 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       // ---- pass 1: row max of the accumulators (plain code: these are the first
       //      reads of the MFMA results)
       // (four independent chains)
+      // (the empty asm keeps each chain step one v_max3: without it the compiler
+      // re-associates the chain into v_max pairs, 3 instructions per 4 values)
       int32_t mx[4] = {S[0][0], S[0][1], S[0][2], S[0][3]};
 #pragma unroll
       for (int kt = 1; kt + 1 < KT; kt += 2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx[r] = max(mx[r], max(S[kt][r], S[kt + 1][r]));  // v_max3
+        for (int r = 0; r < 4; ++r) {
+          mx[r] = max(mx[r], max(S[kt][r], S[kt + 1][r]));  // v_max3
+          asm volatile("" : "+v"(mx[r]));
+        }
       if ((KT & 1) == 0)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx[r] = max(mx[r], S[KT - 1][r]);
@@ -430,10 +445,12 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) O[ft] = v4i{0, 0, 0, 0};
         v4i vcur[FT], vnxt[FT];
-        read_vt<D, FT>(vbase, vtr, vcur);
+        uint32_t va[FT][2];
+        vt_addr<FT>(vbase, vtr, va);
+        read_vt<FT>(va, 0, vcur);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          if (ks + 1 < KS) read_vt<D, FT>(vbase + (ks + 1) * 64 * D, vtr, vnxt);
+          if (ks + 1 < KS) read_vt<FT>(va, (ks + 1) * 64 * D, vnxt);
           v4i pop;
           if (ks * 4 + 3 < KT && p.p_u24) {
             p16_pack24(S[ks * 4], S[ks * 4 + 1], S[ks * 4 + 2], S[ks * 4 + 3], F, pop);
@@ -470,10 +487,12 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) O0[ft] = O1[ft] = v4i{0, 0, 0, 0};
           v4i vcur[FT], vnxt[FT];
-          read_vt<D, FT>(vbase, vtr, vcur);
+          uint32_t va[FT][2];
+          vt_addr<FT>(vbase, vtr, va);
+          read_vt<FT>(va, 0, vcur);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) read_vt<D, FT>(vbase + (ks + 1) * 64 * D, vtr, vnxt);
+            if (ks + 1 < KS) read_vt<FT>(va, (ks + 1) * 64 * D, vnxt);
             v4i plo, phi;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
