@@ -286,6 +286,38 @@ __device__ __forceinline__ int32_t med3_i32(int32_t x, int32_t lo, int32_t hi) {
 //     and 127 * 2^c + b < 2^31 keep the product exact.
 constexpr int RQ_WIDE = 0, RQ_MULHI = 1, RQ_WIN = 2;
 
+// RQ_WIN's last step for one 16-column chunk: the 16 products t[j][i]
+// (column 4 j + i) shifted right by c land as bytes i of the words w[j]
+// through the SDWA destination select, byte-major over the four words: a
+// write that keeps the other bytes reads the old word without an interlock,
+// so two such writes to one word need other instructions between them.  The
+// closing s_nop covers the same for the first later reader.
+__device__ __forceinline__ void ln_shift_pack16(const int32_t (&t)[4][4], int32_t c, v4i& w) {
+  int32_t w0, w1, w2, w3;
+  asm("v_ashrrev_i32_sdwa %0, %20, %4 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %1, %20, %8 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %2, %20, %12 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %3, %20, %16 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %0, %20, %5 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %1, %20, %9 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %2, %20, %13 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %3, %20, %17 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %0, %20, %6 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %1, %20, %10 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %2, %20, %14 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %3, %20, %18 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %0, %20, %7 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %1, %20, %11 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %2, %20, %15 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_ashrrev_i32_sdwa %3, %20, %19 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "s_nop 4"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+      : "v"(t[0][0]), "v"(t[0][1]), "v"(t[0][2]), "v"(t[0][3]), "v"(t[1][0]), "v"(t[1][1]),
+        "v"(t[1][2]), "v"(t[1][3]), "v"(t[2][0]), "v"(t[2][1]), "v"(t[2][2]), "v"(t[2][3]),
+        "v"(t[3][0]), "v"(t[3][1]), "v"(t[3][2]), "v"(t[3][3]), "s"(c));
+  w = v4i{w0, w1, w2, w3};
+}
+
 // gamma and beta sit in LDS, one copy per block, laid out chunk-major: entry
 // ((k * 4 + j) * G + lane) holds the 4 columns 16 * (lane + G * k) + 4 j ..,
 // so that the 16-byte reads of consecutive lanes hit consecutive banks
@@ -370,6 +402,7 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
         bk[j] = reinterpret_cast<const v4i*>(ln_aff)[(k * 4 + j) * G + gl];
         gk[j] = reinterpret_cast<const v4i*>(ln_aff)[NENT + (k * 4 + j) * G + gl];
       }
+      int32_t tw[4][4];  // RQ_WIN: the products before the final shift
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int32_t w = d[k][j];
@@ -385,7 +418,10 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
           if constexpr (RQ == RQ_WIN) {
             const int32_t ys = mad24_sat(nrm, gv, bv);
             const int32_t yc = med3_i32(ys, ylo, p.yhi);
-            y = __mul24(yc, p.b) >> p.c;  // in [-127, 127] by the choice of bounds
+            // (yc b) >> c lies in [-127, 127] by the choice of bounds; the shift
+            // and the byte packing happen in ln_shift_pack16
+            tw[j][i] = __mul24(yc, p.b);
+            continue;
           } else if constexpr (RQ == RQ_MULHI) {
             const int32_t ys = mad24_sat(nrm, gv, bv);
             y = clamp127(__mulhi(ys, p.bm));
@@ -398,6 +434,7 @@ __global__ __launch_bounds__(kLnThreads) void iqln_fwd(LnDev p) {
         }
         o[j] = (int32_t)res;
       }
+      if constexpr (RQ == RQ_WIN) ln_shift_pack16(tw, p.c, o);
       if (rv && col < p.cols) __builtin_amdgcn_raw_buffer_store_b128(o, orr, row * p.cols + col, 0, 0);
       // one chunk's gamma/beta reads at a time: keeps the register count low
       __builtin_amdgcn_sched_barrier(0);
