@@ -146,6 +146,43 @@ __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[
 // scalar registers; the output tensor of a lane's chunk is picked by selects.
 constexpr int kEpPitch = 16 * 4 + 16;  // (16 TN = 64) bytes + 16 of padding
 
+// Window path, four 4-column blocks at once: byte r of word b is
+// floor(yc[b][r] m / 2^32) (v_mul_hi_i32_i24 with an SDWA byte destination,
+// the clamped accumulator and m both within 24 signed bits), written
+// byte-major over the four words: a write that keeps the other bytes reads
+// the old word without an interlock, so two such writes to one word need
+// other instructions between them; the closing s_nop covers the first later
+// reader.  The clamps before it are plain code, the first readers of the MFMA
+// results.
+__device__ __forceinline__ void w24_pack16(const int32_t (&yc)[4][4], int32_t m, uint32_t (&w)[4]) {
+  uint32_t w0, w1, w2, w3;
+  asm("v_mul_hi_i32_i24_sdwa %0, %4, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %8, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %12, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %16, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %0, %5, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %9, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %13, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %17, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %0, %6, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %10, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %14, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %18, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %0, %7, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %11, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %15, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %19, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "s_nop 4"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+      : "v"(yc[0][0]), "v"(yc[0][1]), "v"(yc[0][2]), "v"(yc[0][3]), "v"(yc[1][0]), "v"(yc[1][1]),
+        "v"(yc[1][2]), "v"(yc[1][3]), "v"(yc[2][0]), "v"(yc[2][1]), "v"(yc[2][2]), "v"(yc[2][3]),
+        "v"(yc[3][0]), "v"(yc[3][1]), "v"(yc[3][2]), "v"(yc[3][3]), "v"(m));
+  w[0] = w0;
+  w[1] = w1;
+  w[2] = w2;
+  w[3] = w3;
+}
+
 template <int TM, int TN, bool W24>
 __device__ __forceinline__ void store_tile_lds(const LinParams& p, const v4i (&acc)[TN][TM],
                                                int8_t* scr, int m_w, int n_w, int li, int g,
@@ -157,9 +194,25 @@ __device__ __forceinline__ void store_tile_lds(const LinParams& p, const v4i (&a
   for (int a = 0; a < TN; ++a) {
     const int n = n_w + 16 * a;
     const int which = qkv ? (n >= p.width) + (n >= 2 * p.width) : 0;
+    if constexpr (W24 && TM == 4) {
+      const int32_t lo = pick3(which, p.ylo[0], p.ylo[1], p.ylo[2]);
+      const int32_t hi = pick3(which, p.yhi[0], p.yhi[1], p.yhi[2]);
+      const int32_t m = pick3(which, p.bm24[0], p.bm24[1], p.bm24[2]);
+      int32_t yc[4][4];
 #pragma unroll
-    for (int b = 0; b < TM; ++b)
-      *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = requant4<W24>(p, which, acc[a][b]);
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          yc[b][r] = __builtin_elementwise_max(__builtin_elementwise_min(acc[a][b][r], hi), lo);
+      uint32_t w[4];
+      w24_pack16(yc, m, w);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = w[b];
+    } else {
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = requant4<W24>(p, which, acc[a][b]);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS (one wave: in order)
   // lane chunk k: row lane / TN + (64 / TN) k of the block, column group lane % TN
