@@ -70,6 +70,14 @@ extern "C" {
 #define IQATTN_LIS_VALU 0
 #define IQATTN_LIS_MFMA 1
 
+/* Layouts of the output tensor:
+ * HEADS:  [batch][heads][seq_len][head_dim], the layout of Q, K and V;
+ * TOKENS: [batch][seq_len][heads][head_dim], i.e. rows of heads * head_dim
+ *         features per token: the [tokens][features] input of the output
+ *         projection, with no transpose in between.                          */
+#define IQATTN_OUT_HEADS  0
+#define IQATTN_OUT_TOKENS 1
+
 #define IQATTN_MAX_SEQ 640       /* largest N of the fused register-resident kernel */
 
 /* Parameters of one attention shape.  All values are plain integers.
@@ -84,7 +92,8 @@ extern "C" {
  *   intdiv_m >= 2^lis_bits - 1 and lis_engine IQATTN_LIS_VALU or
  *   IQATTN_LIS_MFMA (ignored for Shiftmax);
  *   rel_bias == NULL and window == 0, or rel_bias != NULL, window >= 1,
- *   seq_len == window * window and |rel_bias[.]| <= 2^30.              */
+ *   seq_len == window * window and |rel_bias[.]| <= 2^30;
+ *   out_layout IQATTN_OUT_HEADS or IQATTN_OUT_TOKENS.                    */
 typedef struct iqattn_params {
   int32_t batch, heads, seq_len, head_dim;
   int32_t qk_b, qk_c;        /* dyadic pair of Q.K^T -> int8 logits            */
@@ -97,6 +106,7 @@ typedef struct iqattn_params {
   int32_t lis_bits;          /* LIS code bits                                   */
   int32_t lis_engine;        /* IQATTN_LIS_VALU or IQATTN_LIS_MFMA               */
   int32_t window;            /* w when rel_bias != NULL, else 0                 */
+  int32_t out_layout;        /* IQATTN_OUT_HEADS or IQATTN_OUT_TOKENS           */
   const int32_t* rel_bias;   /* HOST pointer, [heads][(2w-1)^2] int32, or NULL;
                                 copied by iqattn_create                         */
 } iqattn_params;
@@ -112,9 +122,10 @@ int iqattn_create(const iqattn_params* p, iqattn_ctx** out);
 
 /* Enqueue the fused attention on `hip_stream` (a hipStream_t; NULL = the
  * null stream) of the device the context was created on.  q, k, v (inputs)
- * and out (output) are caller-owned device pointers to contiguous
- * [batch][heads][seq_len][head_dim] int8 tensors, 16-byte aligned; out must
- * not overlap the inputs.  Asynchronous: no allocation, no host
+ * are caller-owned device pointers to contiguous [batch][heads][seq_len]
+ * [head_dim] int8 tensors and out (output) to a contiguous int8 tensor of the
+ * same size in the context's out_layout, all 16-byte aligned; out must not
+ * overlap the inputs.  Asynchronous: no allocation, no host
  * synchronisation.  Returns IQATTN_E_NULL / IQATTN_E_ALIGN for bad pointers
  * (checked before launch) and IQATTN_E_LAUNCH when the launch fails; out is
  * undefined after an error.  A context may be used by several streams at once. */

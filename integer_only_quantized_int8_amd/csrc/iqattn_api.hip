@@ -71,6 +71,7 @@ int validate(const iqattn_params* p) {
     if (p->intdiv_m < (1 << p->lis_bits) - 1) return IQATTN_E_INVAL;
     if (p->lis_engine != IQATTN_LIS_VALU && p->lis_engine != IQATTN_LIS_MFMA) return IQATTN_E_INVAL;
   }
+  if (p->out_layout != IQATTN_OUT_HEADS && p->out_layout != IQATTN_OUT_TOKENS) return IQATTN_E_INVAL;
   if (p->rel_bias == NULL) {
     if (p->window != 0) return IQATTN_E_INVAL;
   } else {
@@ -269,6 +270,7 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   c->dp.bias = c->bias;
   c->dp.heads = p->heads;
   c->dp.n = N;
+  c->dp.out_tok = p->out_layout == IQATTN_OUT_TOKENS;
   c->dp.units = p->batch * p->heads;
   c->dp.n_full = c->dp.units;
   c->dp.n_items = c->dp.units;

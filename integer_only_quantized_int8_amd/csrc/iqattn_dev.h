@@ -34,6 +34,7 @@ struct DevParams {
   const uint32_t* exp_tab;   // [256] e(-idx), or e(-idx) << e_shift for the fast kernels
   const int32_t* bias;       // [heads][Np][Np] expanded, query-major, or null
   int32_t heads, n, units;
+  int32_t out_tok;           // output [B][N][H][d] (1) or [B][H][N][d] (0)
   int32_t n_full;            // work items [0, n_full) are whole heads, later items quarter heads
   int32_t n_items;           // whole heads plus quarter-head items (fast kernels)
   int32_t qk_b, qk_c, pv_b, pv_c;
@@ -49,6 +50,17 @@ struct DevParams {
 };
 
 typedef void (*KernelFn)(DevParams);
+
+// Byte offset of head u's row 0 in the output and the byte distance between
+// its rows: [B][H][N][d] (u N d, d) or [B][N][H][d] ((b N H + h) d, H d) for
+// u = b H + h.
+__device__ __forceinline__ int64_t out_head_base(const DevParams& p, int u, int D) {
+  return p.out_tok ? ((int64_t)(u / p.heads) * p.n * p.heads + (u % p.heads)) * D
+                   : (int64_t)u * p.n * D;
+}
+__device__ __forceinline__ int32_t out_row_stride(const DevParams& p, int D) {
+  return p.out_tok ? p.heads * D : D;
+}
 
 // ---------------------------------------------------------------- arithmetic
 // floor((b * x) / 2^c) saturated to [-127, 127]; 64-bit product.

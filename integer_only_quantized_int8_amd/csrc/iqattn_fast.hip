@@ -335,7 +335,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
     // Query rows past N are clamped to N - 1 for every load, bias read and
     // store: such a lane computes query N - 1 exactly and stores the same bytes.
     const __amdgpu_buffer_rsrc_t qres = buf_rsrc(p.q + hbase, (uint32_t)(N * D));
-    const __amdgpu_buffer_rsrc_t ores = buf_rsrc(p.out + hbase, (uint32_t)(N * D));
+    // output rows of this head: `ostride` bytes apart (head-major or token-major)
+    const int ostride = out_row_stride(p, D);
+    const __amdgpu_buffer_rsrc_t ores =
+        buf_rsrc(p.out + out_head_base(p, u, D), (uint32_t)((N - 1) * ostride + D));
 
     {
       const int qrow = min(qt * 16 + li, N - 1);
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
         }
         // lane holds features 16 ft + 4 g + r of query qrow
-        store_out<FT>(p, O, ores, qrow * D + 4 * g);
+        store_out<FT>(p, O, ores, qrow * ostride + 4 * g);
       } else {
         // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code
         const int32_t Fl = p.lis_f;
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
             for (int r = 0; r < 4; ++r) O0[ft][r] = -(O0[ft][r] + (O1[ft][r] << 8));
-          store_out<FT>(p, O0, ores, qrow * D + 4 * g);
+          store_out<FT>(p, O0, ores, qrow * ostride + 4 * g);
         } else {
           // ---- VALU P.V: lane owns feature t of QPL queries; the wave's shifts
           //      go through LDS one 16-key tile at a time (16 keys x 16 queries)
@@ -554,12 +557,12 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 #pragma unroll
             for (int i = 0; i < QPL; ++i)
               __builtin_amdgcn_raw_buffer_store_b8((uint8_t)clamp127(mulhi_i32(o[i], p.pv_bm)), ores,
-                                                   min(qt * 16 + qsub + i, N - 1) * D + t, 0, 0);
+                                                   min(qt * 16 + qsub + i, N - 1) * ostride + t, 0, 0);
           } else {
 #pragma unroll
             for (int i = 0; i < QPL; ++i)
               __builtin_amdgcn_raw_buffer_store_b8((uint8_t)requant_i8(o[i], p.pv_b, p.pv_c), ores,
-                                                   min(qt * 16 + qsub + i, N - 1) * D + t, 0, 0);
+                                                   min(qt * 16 + qsub + i, N - 1) * ostride + t, 0, 0);
           }
         }
       }

@@ -49,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void iqattn_generic(DevParams p) {
   int32_t* sW = (int32_t*)(sExp + (p.exp_last + 1) * kExpRep);
 
   const int64_t hbase = (int64_t)u * N * D;
+  int8_t* const gO = p.out + out_head_base(p, u, D);  // output rows ostride bytes apart
+  const int64_t ostride = out_row_stride(p, D);
   const int8_t* gK = p.k + hbase;
   const int8_t* gV = p.v + hbase;
 
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void iqattn_generic(DevParams p) {
             int32_t y = requant_i8(O[ft][r], p.pv_b, p.pv_c);
             word |= ((uint32_t)y & 0xffu) << (8 * r);
           }
-          *(uint32_t*)(p.out + hbase + (int64_t)qrow * D + ft * 16 + 4 * g) = word;
+          *(uint32_t*)(gO + qrow * ostride + ft * 16 + 4 * g) = word;
         }
       }
     } else {
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void iqattn_generic(DevParams p) {
 #pragma unroll
       for (int i = 0; i < QPL; ++i) {
         const int qi = qt * 16 + qsub + i;
-        if (qi < N) p.out[hbase + (int64_t)qi * D + t] = (int8_t)requant_i8(o[i], p.pv_b, p.pv_c);
+        if (qi < N) gO[qi * ostride + t] = (int8_t)requant_i8(o[i], p.pv_b, p.pv_c);
       }
     }
   }

@@ -27,6 +27,8 @@ IQATTN_E_ALIGN = -6
 IQATTN_E_DEVICE = -7
 IQATTN_SHIFTMAX = 0
 IQATTN_LIS = 1
+IQATTN_OUT_HEADS = 0
+IQATTN_OUT_TOKENS = 1
 IQATTN_LIS_VALU = 0
 IQATTN_LIS_MFMA = 1
 IQATTN_MAX_SEQ = 640
@@ -43,8 +45,8 @@ EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerro
 class iqattn_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "batch", "heads", "seq_len", "head_dim", "qk_b", "qk_c", "pv_b", "pv_c", "i0",
-        "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "lis_engine", "window")] + \
-        [("rel_bias", C.POINTER(C.c_int32))]
+        "exp_frac_bits", "intdiv_m", "k_out", "variant", "lis_bits", "lis_engine", "window",
+        "out_layout")] + [("rel_bias", C.POINTER(C.c_int32))]
 
 
 class iqlinear_params(C.Structure):
@@ -130,7 +132,7 @@ def make_params(shape, params: Dict[str, object]):
     p = iqattn_params()
     p.batch, p.heads, p.seq_len, p.head_dim = int(B), int(H), int(N), int(d)
     for name in ("qk_b", "qk_c", "pv_b", "pv_c", "i0", "exp_frac_bits", "intdiv_m", "k_out",
-                 "variant", "lis_bits", "lis_engine", "window"):
+                 "variant", "lis_bits", "lis_engine", "window", "out_layout"):
         setattr(p, name, int(params.get(name, 0) or 0))
     keep = None
     rb = params.get("rel_bias")
@@ -180,11 +182,16 @@ class IQAttn:
 
     def __init__(self, shape, params: Dict[str, object]):
         self.shape = tuple(int(x) for x in shape)
+        self.out_layout = int(params.get("out_layout", IQATTN_OUT_HEADS) or 0)
+        B, H, N, d = self.shape
+        self.out_shape = (B, N, H, d) if self.out_layout == IQATTN_OUT_TOKENS else self.shape
         p, keep = make_params(self.shape, params)
         self.ctx = iqattn_create(p)
         del keep
 
     def forward(self, q, k, v, out=None, stream=None):
+        """out: [B, H, N, d], or [B, N, H, d] for out_layout IQATTN_OUT_TOKENS
+        (any contiguous int8 device tensor of that many elements)."""
         import torch
         for name, t in (("q", q), ("k", k), ("v", v)):
             if t.dtype != torch.int8 or not t.is_cuda or not t.is_contiguous() \
@@ -192,7 +199,10 @@ class IQAttn:
                 raise ValueError(f"{name} must be a contiguous int8 device tensor of shape "
                                  f"{self.shape}")
         if out is None:
-            out = torch.empty_like(q)
+            out = torch.empty(self.out_shape, dtype=torch.int8, device=q.device)
+        elif out.dtype != torch.int8 or not out.is_cuda or not out.is_contiguous() \
+                or out.numel() != q.numel():
+            raise ValueError(f"out must be a contiguous int8 device tensor of shape {self.out_shape}")
         iqattn_forward(self.ctx, q, k, v, out, stream)
         return out
 

@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
     for name in ("IQATTN_OK", "IQATTN_E_INVAL", "IQATTN_E_SHAPE", "IQATTN_E_ALLOC",
                  "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
                  "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_LIS_VALU", "IQATTN_LIS_MFMA",
-                 "IQATTN_MAX_SEQ"):
+                 "IQATTN_OUT_HEADS", "IQATTN_OUT_TOKENS", "IQATTN_MAX_SEQ"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(IQ, name), name
     text = open(os.path.join(ROOT, "include", "iqlinear.h")).read()
@@ -80,6 +80,8 @@ def _create_rc(lib, shape, **over):
     ((1, 1, 16, 64), {"variant": 1, "lis_engine": 2}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"variant": 1, "lis_engine": -1}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"window": 4}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"out_layout": 2}, IQ.IQATTN_E_INVAL),
+    ((1, 1, 16, 64), {"out_layout": -1}, IQ.IQATTN_E_INVAL),
     ((1, 1, 16, 64), {"window": 3, "rel_bias": np.zeros((1, 25), np.int32)}, IQ.IQATTN_E_SHAPE),
     ((1, 1, 16, 64), {"window": 4, "rel_bias": np.full((1, 49), (1 << 30) + 1, np.int32)},
      IQ.IQATTN_E_INVAL),
@@ -224,3 +226,39 @@ def test_linattn_null_arguments(lib):
     assert lib.iqlinattn_create(None, None) == IQ.IQATTN_E_NULL
     assert lib.iqlinattn_destroy(None) == IQ.IQATTN_OK
     assert lib.iqlinattn_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL
+
+
+def test_struct_layouts_match_headers():
+    """Every parameter struct of include/*.h has the size and field offsets of
+    its ctypes twin in the binding (a small C program, built in the
+    repository's untracked _build/, prints them)."""
+    import pathlib
+    import subprocess
+    tmp_path = pathlib.Path(ROOT) / "_build" / "layout_check"
+    tmp_path.mkdir(parents=True, exist_ok=True)
+    structs = {
+        "iqattn_params": (IQ.iqattn_params, "iqattn.h"),
+        "iqlinear_params": (IQ.iqlinear_params, "iqlinear.h"),
+        "iqgelu_params": (IQ.iqgelu_params, "iqblock.h"),
+        "iqlayernorm_params": (IQ.iqlayernorm_params, "iqblock.h"),
+        "iqlinattn_params": (IQ.iqlinattn_params, "iqlinattn.h"),
+    }
+    lines = ["#include <stdio.h>", "#include <stddef.h>"]
+    lines += sorted({f'#include "{h}"' for _, h in structs.values()})
+    lines.append("int main(void) {")
+    for name, (cls, _) in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    exe = tmp_path / "layout"
+    src.write_text("\n".join(lines) + "\n")
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-o",
+                           str(exe), str(src)])
+    out = subprocess.check_output([str(exe)]).decode().split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for name, (cls, _) in structs.items():
+        assert got[(name, "size")] == C.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert got[(name, field)] == getattr(cls, field).offset, (name, field)

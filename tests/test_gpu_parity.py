@@ -194,3 +194,74 @@ def test_empty_batch_and_alignment_errors(torch_dev):
         att.forward(mis, mis, mis)
     assert ei.value.code == IQ.IQATTN_E_ALIGN
     att.close()
+
+
+@pytest.mark.parametrize("spec,engine", [
+    (dict(W.CONFIGS[0]), None),                                   # specialised, 13 key tiles
+    (dict(W.CONFIGS[3], batch=8), None),                          # windowed, bias, d = 32
+    (dict(W.CONFIGS[4], batch=1, heads=3), 0),                    # LIS, VALU P.V, 577 keys
+    (dict(W.CONFIGS[4], batch=1, heads=3), 1),                    # LIS, MFMA P.V
+    (dict(batch=2, heads=3, seq_len=400, head_dim=64), None),     # generic kernel
+    (dict(batch=2, heads=3, seq_len=400, head_dim=32, variant=1), 0),  # generic LIS
+])
+def test_token_major_output(torch_dev, spec, engine):
+    """out_layout IQATTN_OUT_TOKENS writes [B, N, H, d] (rows of H d features
+    per token): the same bytes as the head-major result, transposed."""
+    torch = torch_dev
+    from integer_only_quantized_int8_amd.iqattn import IQAttn, IQATTN_OUT_TOKENS
+    spec = {k: v for k, v in spec.items() if k != "name"}
+    w = W.make_workload(seed=77, **spec)
+    params = dict(w.params, out_layout=IQATTN_OUT_TOKENS)
+    if engine is not None:
+        params["lis_engine"] = engine
+    _say(f"[parity] token-major {w.q.shape} variant={w.params['variant']} engine={engine}")
+    att = IQAttn(w.q.shape, params)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
+    B, H, N, d = w.q.shape
+    buf = torch.full((B * N * H * d + 64,), 99, dtype=torch.int8, device=dev)
+    out = buf[:B * N * H * d].view(B, N, H, d)
+    att.forward(q, k, v, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    att.close()
+    assert np.all(buf[B * N * H * d:].cpu().numpy() == 99), "write past the output"
+    ref = oracle.forward(w.q, w.k, w.v, w.params if engine is None else params)
+    ref = ref.reshape(B, H, N, d).transpose(0, 2, 1, 3)
+    assert np.array_equal(got, ref), f"{np.argwhere(got != ref)[:4].tolist()}"
+
+
+def test_msa_block_without_transposes(torch_dev):
+    """Q/K/V projection (head-split output), attention (token-major output) and
+    output projection chained on the GPU, no reshaping copy in between, against
+    the oracle chain."""
+    torch = torch_dev
+    from integer_only_quantized_int8_amd.iqattn import IQAttn, IQLinear, IQATTN_OUT_TOKENS
+    B, N, H, d = 2, 197, 4, 64
+    C = H * d
+    qkv = W.make_linear(B * N, C, 3 * C, seed=81, qkv_heads=(B, N, H, d))
+    proj = W.make_linear(B * N, C, C, seed=82)
+    att_w = W.make_workload(seed=83, batch=B, heads=H, seq_len=N, head_dim=d)
+    _say("[parity] MSA block: qkv -> attention (token-major) -> proj")
+    dev = torch.device("cuda:0")
+    lq = IQLinear(qkv.params)
+    att = IQAttn((B, H, N, d), dict(att_w.params, out_layout=IQATTN_OUT_TOKENS))
+    lp = IQLinear(proj.params)
+    x = torch.from_numpy(qkv.x).to(dev)
+    wq = torch.from_numpy(qkv.w).to(dev)
+    wp = torch.from_numpy(proj.w).to(dev)
+    q, k, v = lq.forward(x, wq)
+    a = att.forward(q, k, v)                     # [B, N, H, d] = [B N, C] rows
+    y = lp.forward(a.view(B * N, C), wp)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    for o in (lq, att, lp):
+        o.close()
+    # oracle chain
+    P = qkv.params
+    parts = [oracle.linear(qkv.x, qkv.w[i * C:(i + 1) * C], P["b"][i], P["c"][i]) for i in range(3)]
+    heads = [t.reshape(B, N, H, d).transpose(0, 2, 1, 3).copy() for t in parts]
+    o = oracle.forward(heads[0], heads[1], heads[2], att_w.params)
+    tok = o.reshape(B, H, N, d).transpose(0, 2, 1, 3).reshape(B * N, C)
+    ref = oracle.linear(tok, proj.w, proj.params["b"][0], proj.params["c"][0])
+    assert np.array_equal(got, ref)
