@@ -161,6 +161,8 @@ __device__ __forceinline__ void p16_pack24(const v4i& e0, const v4i& e1, const v
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 typedef int32_t v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const int8_t lds_i8;
 typedef __attribute__((address_space(3))) uint32_t lds_u32w;
 
 // buffer_load_dwordx4 ... lds: each lane's 16 bytes at rsrc.base + voffset go to

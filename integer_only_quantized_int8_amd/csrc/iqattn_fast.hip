@@ -57,27 +57,98 @@ __device__ __forceinline__ int vswz(int row) {
   return D == 64 ? (((row >> 2) & 1) | ((row >> 3) & 2)) : (row >> 4) & 1;
 }
 
-// LIS shift w = F - code for the probability Ph (Ph < 2^24):
-// code = F - ilog2r(Ph) clipped to [0, F], Ph = 0 -> code F.  ilog2r(x) is the
+// LIS shift w = F - code of the probability Ph = (f e) >> (M - F).  Ph <= 2^F
+// (e is at most the row sum s and f = floor(2^M / s)), so w = ilog2r(max(Ph, 1))
+// with no clamp: Ph = 0 and Ph = 1 both give code F.  ilog2r(x) is the
 // leading-one index plus the next bit; for x < 2^24 the float conversion is
 // exact, its mantissa's top bit is that next bit, and adding 2^22 to the bit
-// pattern carries it into the exponent.
-__device__ __forceinline__ int32_t lis_shift(uint32_t ph, int32_t F) {
-  const uint32_t bits = __float_as_uint((float)ph) + 0x400000u;
-  return min(max((int32_t)(bits >> 23) - 127, 0), F);
+// pattern carries it into the exponent.  Adding 2^23 more returns the biased
+// exponent plus one, w + 128: w in the low four and the low five bits.
+// (The empty asm keeps the conversion a 32-bit one: without it the compiler
+// sees that ph is the high half of a 64-bit product and converts that as a
+// 64-bit integer, five instructions instead of one.)
+__device__ __forceinline__ uint32_t lis_exp(uint32_t ph) {
+  asm("" : "+v"(ph));
+  return (__float_as_uint((float)max(ph, 1u)) + 0xC00000u) >> 23;
 }
 
-// LIS bit-plane operand bytes of four shifts: plane 0 gets -2^w for w < 8,
-// plane 1 gets -2^(w-8) for w >= 8 (as int8 bytes 0xFF << l).
+// o + (v << w) as one v_lshl_add_u32 (the empty asm keeps every step a single
+// instruction: without it the compiler pairs two shifts into a v_add3_u32, three
+// instructions per two steps)
+__device__ __forceinline__ int32_t shl_add(int32_t v, int32_t w, int32_t o) {
+  int32_t r = (int32_t)(((uint32_t)v << (w & 31)) + (uint32_t)o);
+  asm("" : "+v"(r));
+  return r;
+}
+
+// LIS bit-plane operand bytes of four shifts (w in the low four bits of each
+// word): plane 0 gets -2^w for w < 8, plane 1 gets -2^(w-8) for w >= 8 (as
+// int8 bytes 0xFF << l).
 __device__ __forceinline__ void lis_planes(const v4i& w, int32_t& lo, int32_t& hi) {
   uint32_t y[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)  // 16-bit (plane 1 byte, plane 0 byte)
-    y[r] = (0xFFu << w[r]) & (0xFFu << (w[r] & 8));
+  for (int r = 0; r < 4; ++r) {  // 16-bit (plane 1 byte, plane 0 byte)
+    const uint32_t l = (uint32_t)w[r] & 15u;
+    y[r] = (0xFFu << l) & (0xFFu << (l & 8));
+  }
   const uint32_t t01 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
   const uint32_t t23 = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
   lo = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
   hi = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
+}
+
+// The two bit-plane operand words of sixteen LIS shifts at once (four 16-key
+// tiles of four keys).  Each input holds w (mod 16) in byte 0 and w + 8 (mod
+// 16) in byte 1.  v_lshlrev_b16 shifts by the low four bits of its amount, so
+// the low byte of 0xFF << (w mod 16) is the plane-0 byte (0 for w >= 8) and
+// that of 0xFF << ((w + 8) mod 16) the plane-1 byte (0 for w < 8); the SDWA
+// form takes the amount from byte 0 or byte 1 of the input and writes that low
+// byte straight into byte r of the operand word.  The writes go byte-major
+// (eight instructions between writes to one word) and end with the wait
+// states an MFMA reading the words needs, as in p16_pack24.
+__device__ __forceinline__ void lis_planes16(const v4i& x0, const v4i& x1, const v4i& x2,
+                                             const v4i& x3, uint32_t ff, v4i& lo, v4i& hi) {
+  uint32_t l0, l1, l2, l3, h0, h1, h2, h3;
+  asm(
+      "v_lshlrev_b16_sdwa %0, %8, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %1, %12, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %2, %16, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %3, %20, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %4, %8, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %5, %12, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %6, %16, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %7, %20, %24 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %0, %9, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %1, %13, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %2, %17, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %3, %21, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %4, %9, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %5, %13, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %6, %17, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %7, %21, %24 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %0, %10, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %1, %14, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %2, %18, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %3, %22, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %4, %10, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %5, %14, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %6, %18, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %7, %22, %24 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %0, %11, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %1, %15, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %2, %19, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %3, %23, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %4, %11, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %5, %15, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %6, %19, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "v_lshlrev_b16_sdwa %7, %23, %24 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1 src1_sel:WORD_0\n\t"
+      "s_nop 4"
+      : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3), "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3)
+      : "v"(x0[0]), "v"(x0[1]), "v"(x0[2]), "v"(x0[3]), "v"(x1[0]), "v"(x1[1]), "v"(x1[2]),
+        "v"(x1[3]), "v"(x2[0]), "v"(x2[1]), "v"(x2[2]), "v"(x2[3]), "v"(x3[0]), "v"(x3[1]),
+        "v"(x3[2]), "v"(x3[3]), "v"(ff));
+  lo = v4i{(int32_t)l0, (int32_t)l1, (int32_t)l2, (int32_t)l3};
+  hi = v4i{(int32_t)h0, (int32_t)h1, (int32_t)h2, (int32_t)h3};
 }
 
 // One work item: head u (-1 past the end) and its query tiles qt0, qt0 + qstep,
@@ -477,14 +548,16 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
         // lane holds features 16 ft + 4 g + r of query qrow
         store_out<FT>(p, O, ores, qrow * ostride + 4 * g);
       } else {
-        // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code
-        const int32_t Fl = p.lis_f;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) S[kt][r] = lis_shift(mulhi_u32((uint32_t)S[kt][r], F), Fl);
-
+        // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code as
+        //      w + 128 (VALU engine: the amount of a 32-bit shift, formed one
+        //      16-key tile at a time in the P.V loop) or as the two plane-shift
+        //      bytes w + 128 and w + 136 (MFMA engine)
         if (VAR == kFastLisMfma) {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              S[kt][r] = (int32_t)(lis_exp(mulhi_u32((uint32_t)S[kt][r], F)) * 257u + 2048u);
           // ---- o = -(O_0 + 256 O_1), O_h = V^T . (plane h of -2^w)^T
           v4i O0[FT], O1[FT];
 #pragma unroll
@@ -497,13 +570,17 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) read_vt<FT>(va, (ks + 1) * 64 * D, vnxt);
             v4i plo, phi;
+            if (ks * 4 + 3 < KT) {
+              lis_planes16(S[ks * 4], S[ks * 4 + 1], S[ks * 4 + 2], S[ks * 4 + 3], 0xFFu, plo, phi);
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-              const int kt = ks * 4 + tt;
-              int32_t lo_w = 0, hi_w = 0;
-              if (kt < KT) lis_planes(S[kt], lo_w, hi_w);
-              plo[tt] = lo_w;
-              phi[tt] = hi_w;
+              for (int tt = 0; tt < 4; ++tt) {
+                const int kt = ks * 4 + tt;
+                int32_t lo_w = 0, hi_w = 0;
+                if (kt < KT) lis_planes(S[kt], lo_w, hi_w);
+                plo[tt] = lo_w;
+                phi[tt] = hi_w;
+              }
             }
 #pragma unroll
             for (int ft = 0; ft < FT; ++ft) {
@@ -520,49 +597,72 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
             for (int r = 0; r < 4; ++r) O0[ft][r] = -(O0[ft][r] + (O1[ft][r] << 8));
           store_out<FT>(p, O0, ores, qrow * ostride + 4 * g);
         } else {
-          // ---- VALU P.V: lane owns feature t of QPL queries; the wave's shifts
-          //      go through LDS one 16-key tile at a time (16 keys x 16 queries)
-          constexpr int QPL = 16 * D / 64;
-          const int t = lane % D;
-          const int qsub = (lane / D) * QPL;
+          // ---- VALU P.V: lane owns 4 queries x NF = D / 16 features (lanes
+          //      16 qg + fg: queries 4 qg.., features NF fg..); the wave's shifts
+          //      go through LDS one 16-key tile at a time (16 keys x 16
+          //      queries).  Per key a lane reads its 4 shifts (one b128, the
+          //      same for the 16 lanes of its query group) and its NF V bytes
+          //      for 4 NF shift-adds: half the LDS bytes per shift-add of one
+          //      query per lane at D = 64
+          constexpr int NF = D / 16;
+          const int fg = lane & 15, qg = lane >> 4;
+          const int q0 = 4 * qg, f0 = NF * fg;
           int32_t* sWw = sW + wave * 256;
-          int32_t o[QPL];
+          // this lane's column block of the shift rows, held in a VGPR (the empty
+          // asm): a wave-uniform address would be formed in SGPRs and copied to a
+          // VGPR for every read instead of riding in the reads' offset field
+          uint32_t wcol = lds_addr(sWw + q0);
+          asm volatile("" : "+v"(wcol));
+          int32_t o[4][NF];
 #pragma unroll
-          for (int i = 0; i < QPL; ++i) o[i] = 0;
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) o[i][f] = 0;
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sWw[(4 * g + r) * 16 + li] = S[kt][r];
+            for (int r = 0; r < 4; ++r)
+              sWw[(4 * g + r) * 16 + li] = (int32_t)lis_exp(mulhi_u32((uint32_t)S[kt][r], F));
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll 4
             for (int jj = 0; jj < 16; ++jj) {
               const int row = kt * 16 + jj;  // rows >= N are zero
-              const int32_t vj = (int32_t)sV[row * D + (t ^ (vswz<D>(row) << 4))];
-              const v4i* wrow = (const v4i*)(sWw + jj * 16 + qsub);
+              // f0.. f0 + NF - 1 lie in one 16-byte chunk, which the swizzle moves
+              // whole; one sign-extending byte read per feature (volatile: merged
+              // into one dword read, each byte would cost an extract instruction)
+              const volatile lds_i8* vrow =
+                  (const volatile lds_i8*)(uintptr_t)lds_addr(sV + row * D + (f0 ^ (vswz<D>(row) << 4)));
+              int32_t v[NF];
 #pragma unroll
-              for (int i4 = 0; i4 < QPL / 4; ++i4) {
-                const v4i w4 = wrow[i4];
+              for (int f = 0; f < NF; ++f) v[f] = (int32_t)vrow[f];
+              const v4i w4 = *(lds_v4i*)(uintptr_t)(wcol + (uint32_t)(jj * 16) * 4u);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[4 * i4 + r] += (int32_t)((uint32_t)vj << w4[r]);
-              }
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int f = 0; f < NF; ++f) o[i][f] = shl_add(v[f], w4[i], o[i][f]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (p.pv_fast) {
+          // requantise, pack the NF bytes of a query, one store per query
 #pragma unroll
-            for (int i = 0; i < QPL; ++i)
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)clamp127(mulhi_i32(o[i], p.pv_bm)), ores,
-                                                   min(qt * 16 + qsub + i, N - 1) * ostride + t, 0, 0);
-          } else {
+          for (int i = 0; i < 4; ++i) {
+            uint32_t y[NF];
 #pragma unroll
-            for (int i = 0; i < QPL; ++i)
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)requant_i8(o[i], p.pv_b, p.pv_c), ores,
-                                                   min(qt * 16 + qsub + i, N - 1) * ostride + t, 0, 0);
+            for (int f = 0; f < NF; ++f)
+              y[f] = (uint32_t)(p.pv_fast ? clamp127(mulhi_i32(o[i][f], p.pv_bm))
+                                          : requant_i8(o[i][f], p.pv_b, p.pv_c));
+            const int dst = min(qt * 16 + q0 + i, N - 1) * ostride + f0;
+            if (NF == 4)
+              __builtin_amdgcn_raw_buffer_store_b32(pack4_lowbytes(y[0], y[1], y[2], y[3]), ores,
+                                                    dst, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  (uint16_t)__builtin_amdgcn_perm(y[NF - 1], y[0], 0x0c0c0400u), ores, dst, 0, 0);
           }
         }
       }
