@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA
+# VALU lane rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one 32-bit integer
+# operation per lane and cycle (a wave64 instruction occupies a SIMD 4 cycles)
+VALU_LANE_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 KERNEL_DIR = os.path.join(ROOT, "integer_only_quantized_int8_amd", "csrc")
 METRIC = "integer-only MSA int8 TOPS + % roofline, B=128 H=12 N=197 d=64, 1 MI355X"
 
@@ -462,6 +465,19 @@ def main():
                                    "peak_tops": MFMA_I8_PEAK_TOPS,
                                    "frac": round(ops / (kern_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}},
     }
+    if w.params["variant"] == 1 and int(w.params.get("lis_engine", 0)) == 0:
+        # the LIS BitShift P.V on the VALU: one shift-add per (query, key,
+        # feature), N^2 d per head, bounds this launch (HBM and MFMA stay listed)
+        shifts = float(N) * N * d * heads
+        alu = shifts / (kern_ms * 1e-3) / 1e12
+        hbm = result["roofline"]
+        result["roofline"] = {
+            "bound": "alu", "achieved": round(alu, 2), "peak": round(VALU_LANE_PEAK_TOPS, 2),
+            "unit": "TOP/s", "frac": round(alu / VALU_LANE_PEAK_TOPS, 4), "traffic": traffic,
+            "algorithmic_shift_adds_per_launch": int(shifts),
+            "hbm": {"achieved_gbs": hbm["achieved"], "peak_gbs": HBM_PEAK_GBS, "frac": hbm["frac"],
+                    "algorithmic_bytes_per_launch": hbm["algorithmic_bytes_per_launch"]},
+            "mfma_int8": hbm["mfma_int8"]}
 
     if not args.no_cpu:
         import oracle
