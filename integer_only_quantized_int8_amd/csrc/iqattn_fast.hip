@@ -335,6 +335,11 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       }
       if (lane == 0) __hip_atomic_store(&ctl_done[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       stage_head<D, R, QLDS>(p, it.u, smem0 + b * BS, lane);
+      // (in effect both flags below are set once K, Q and V are all in: the
+      // compiler puts a vmcnt(0) before every LDS access that follows a direct
+      // load into LDS, the release stores included.  Loaders that set the K/Q
+      // flag first, or kept two items in flight, through flag accesses in asm,
+      // measured slower on every short-row shape.)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(R / 1024));  // K and Q are in LDS
       if (lane == 0) __hip_atomic_store(&ctl_ready[b], j, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       __builtin_amdgcn_s_waitcnt(0);  // and V
