@@ -684,29 +684,36 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 #define IQ_FAST_CASE(D, KT, B, V) \
   if (d == D && kt == KT && bias == B && var == V) return iqattn_fast<D, KT, B, V>;
 
+// every row of up to 256 keys (KT <= 16) for both head sizes and all three back
+// ends, except d = 64 with 14 to 16 key tiles for Shiftmax and LIS MFMA (their
+// 16-wave workgroups would spill registers; the generic kernel runs those);
+// windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); longer
+// rows at N = 257 and N = 577
+#define IQ_FAST_ALL_VAR(D, KT)                 \
+  IQ_FAST_CASE(D, KT, false, kFastShiftmax) \
+  IQ_FAST_CASE(D, KT, false, kFastLisValu)  \
+  IQ_FAST_CASE(D, KT, false, kFastLisMfma)
+#define IQ_FAST_SHORT13(D)                                                                \
+  IQ_FAST_ALL_VAR(D, 1) IQ_FAST_ALL_VAR(D, 2) IQ_FAST_ALL_VAR(D, 3) IQ_FAST_ALL_VAR(D, 4)     \
+  IQ_FAST_ALL_VAR(D, 5) IQ_FAST_ALL_VAR(D, 6) IQ_FAST_ALL_VAR(D, 7) IQ_FAST_ALL_VAR(D, 8)     \
+  IQ_FAST_ALL_VAR(D, 9) IQ_FAST_ALL_VAR(D, 10) IQ_FAST_ALL_VAR(D, 11) IQ_FAST_ALL_VAR(D, 12)  \
+  IQ_FAST_ALL_VAR(D, 13)
+
 KernelFn fast_kernel(int d, int kt, bool bias, int var) {
-  // Shiftmax: the workload shapes and the tile counts the tests use
-  IQ_FAST_CASE(64, 13, false, kFastShiftmax)
-  IQ_FAST_CASE(64, 37, false, kFastShiftmax)
-  IQ_FAST_CASE(64, 1, false, kFastShiftmax)
-  IQ_FAST_CASE(64, 2, false, kFastShiftmax)
-  IQ_FAST_CASE(64, 4, false, kFastShiftmax)
-  IQ_FAST_CASE(64, 12, false, kFastShiftmax)
+  IQ_FAST_SHORT13(64)
+  IQ_FAST_CASE(64, 14, false, kFastLisValu)
+  IQ_FAST_CASE(64, 15, false, kFastLisValu)
+  IQ_FAST_CASE(64, 16, false, kFastLisValu)
+  IQ_FAST_SHORT13(32)
+  IQ_FAST_ALL_VAR(32, 14)
+  IQ_FAST_ALL_VAR(32, 15)
+  IQ_FAST_ALL_VAR(32, 16)
   IQ_FAST_CASE(64, 4, true, kFastShiftmax)
   IQ_FAST_CASE(32, 4, true, kFastShiftmax)
-  IQ_FAST_CASE(32, 4, false, kFastShiftmax)
-  IQ_FAST_CASE(32, 13, false, kFastShiftmax)
-  // Log-Int-Softmax, both P.V engines
-  IQ_FAST_CASE(64, 37, false, kFastLisValu)
-  IQ_FAST_CASE(64, 37, false, kFastLisMfma)
-  IQ_FAST_CASE(64, 1, false, kFastLisValu)
-  IQ_FAST_CASE(64, 1, false, kFastLisMfma)
-  IQ_FAST_CASE(64, 5, false, kFastLisValu)
-  IQ_FAST_CASE(64, 5, false, kFastLisMfma)
-  IQ_FAST_CASE(64, 13, false, kFastLisValu)
-  IQ_FAST_CASE(64, 13, false, kFastLisMfma)
-  IQ_FAST_CASE(32, 4, false, kFastLisValu)
-  IQ_FAST_CASE(32, 4, false, kFastLisMfma)
+  IQ_FAST_CASE(64, 9, true, kFastShiftmax)
+  IQ_FAST_CASE(32, 9, true, kFastShiftmax)
+  IQ_FAST_ALL_VAR(64, 17)
+  IQ_FAST_ALL_VAR(64, 37)
   return nullptr;
 }
 

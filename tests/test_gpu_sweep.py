@@ -53,9 +53,8 @@ def draw_pair(rng, acc_sd, lo_target=2.0, hi_target=100.0, wild=0.25):
 
 # ------------------------------------------------------------------ attention
 
-# (head_dim, key tiles of 16, relative bias, variant) of the specialised
-# kernels: the workload shapes (N = 197, 577, 49 with and without bias) and
-# the short ones
+# (head_dim, key tiles of 16, relative bias, variant) of specialised kernels:
+# the workload shapes (N = 197, 577, 49 with and without bias) and short ones
 SPECIALISED = ([(64, kt, False, 0) for kt in (1, 2, 4, 12, 13, 37)]
                + [(64, 4, True, 0), (32, 4, True, 0), (32, 4, False, 0), (32, 13, False, 0)]
                + [(64, kt, False, 1) for kt in (1, 5, 13, 37)] + [(32, 4, False, 1)])
