@@ -686,7 +686,8 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 
 // every row of up to 256 keys (KT <= 16) for both head sizes and all three back
 // ends, except d = 64 with 14 to 16 key tiles for Shiftmax and LIS MFMA (their
-// 16-wave workgroups would spill registers; the generic kernel runs those);
+// 16-wave workgroups would spill registers) and with 16 for LIS VALU (its three
+// buffers and shift scratch would pass 160 KB of LDS): the generic kernel runs those;
 // windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); longer
 // rows at N = 257 and N = 577
 #define IQ_FAST_ALL_VAR(D, KT)                 \
@@ -703,7 +704,6 @@ KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   IQ_FAST_SHORT13(64)
   IQ_FAST_CASE(64, 14, false, kFastLisValu)
   IQ_FAST_CASE(64, 15, false, kFastLisValu)
-  IQ_FAST_CASE(64, 16, false, kFastLisValu)
   IQ_FAST_SHORT13(32)
   IQ_FAST_ALL_VAR(32, 14)
   IQ_FAST_ALL_VAR(32, 15)
