@@ -688,8 +688,8 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 // ends, except d = 64 with 14 to 16 key tiles for Shiftmax and LIS MFMA (their
 // 16-wave workgroups would spill registers) and with 16 for LIS VALU (its three
 // buffers and shift scratch would pass 160 KB of LDS): the generic kernel runs those;
-// windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); longer
-// rows at N = 257 and N = 577
+// windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); every
+// longer row up to 640 keys (except LIS MFMA at d = 64 past 608 keys)
 #define IQ_FAST_ALL_VAR(D, KT)                 \
   IQ_FAST_CASE(D, KT, false, kFastShiftmax) \
   IQ_FAST_CASE(D, KT, false, kFastLisValu)  \
@@ -700,7 +700,17 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   IQ_FAST_ALL_VAR(D, 9) IQ_FAST_ALL_VAR(D, 10) IQ_FAST_ALL_VAR(D, 11) IQ_FAST_ALL_VAR(D, 12)  \
   IQ_FAST_ALL_VAR(D, 13)
 
+#define IQ_FAST_LONG(D)                                                                    \
+  IQ_FAST_ALL_VAR(D, 17) IQ_FAST_ALL_VAR(D, 18) IQ_FAST_ALL_VAR(D, 19) IQ_FAST_ALL_VAR(D, 20)  \
+  IQ_FAST_ALL_VAR(D, 21) IQ_FAST_ALL_VAR(D, 22) IQ_FAST_ALL_VAR(D, 23) IQ_FAST_ALL_VAR(D, 24)  \
+  IQ_FAST_ALL_VAR(D, 25) IQ_FAST_ALL_VAR(D, 26) IQ_FAST_ALL_VAR(D, 27) IQ_FAST_ALL_VAR(D, 28)  \
+  IQ_FAST_ALL_VAR(D, 29) IQ_FAST_ALL_VAR(D, 30) IQ_FAST_ALL_VAR(D, 31) IQ_FAST_ALL_VAR(D, 32)  \
+  IQ_FAST_ALL_VAR(D, 33) IQ_FAST_ALL_VAR(D, 34) IQ_FAST_ALL_VAR(D, 35) IQ_FAST_ALL_VAR(D, 36)  \
+  IQ_FAST_ALL_VAR(D, 37) IQ_FAST_ALL_VAR(D, 38) IQ_FAST_ALL_VAR(D, 39) IQ_FAST_ALL_VAR(D, 40)
+
 KernelFn fast_kernel(int d, int kt, bool bias, int var) {
+  // (d = 64, LIS MFMA at 609-640 keys would spill registers: generic kernel)
+  if (d == 64 && kt >= 39 && var == kFastLisMfma) return nullptr;
   IQ_FAST_SHORT13(64)
   IQ_FAST_CASE(64, 14, false, kFastLisValu)
   IQ_FAST_CASE(64, 15, false, kFastLisValu)
@@ -712,8 +722,8 @@ KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   IQ_FAST_CASE(32, 4, true, kFastShiftmax)
   IQ_FAST_CASE(64, 9, true, kFastShiftmax)
   IQ_FAST_CASE(32, 9, true, kFastShiftmax)
-  IQ_FAST_ALL_VAR(64, 17)
-  IQ_FAST_ALL_VAR(64, 37)
+  IQ_FAST_LONG(64)
+  IQ_FAST_LONG(32)
   return nullptr;
 }
 
