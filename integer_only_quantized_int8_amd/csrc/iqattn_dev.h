@@ -247,14 +247,22 @@ constexpr int fast_region_bytes(int d, int kt) { return ((kt * 16 * d + 1023) / 
 // apart: the older one's waves win the issue arbitration and the younger one
 // finishes alone).  Longer rows (about 250 VGPRs per lane) use 3 compute waves
 // and one (V, K) buffer, two workgroups per CU.
+// Rows of 209 to 256 keys (14 to 16 tiles) run 11 compute waves over three
+// buffers: at 16 waves their accumulators would not fit the registers, and at
+// d = 64 four buffers would not fit the LDS.
 constexpr bool fast_big(int kt, bool bias) { return kt <= 16; }
+constexpr bool fast_mid(int kt, bool bias) { return kt >= 14 && kt <= 16; }
 constexpr int fast_nbuf(int kt, bool bias, int var) {
-  return fast_big(kt, bias) ? (var == kFastLisValu ? 3 : 4) : 1;
+  return fast_big(kt, bias) ? (var == kFastLisValu || fast_mid(kt, bias) ? 3 : 4) : 1;
 }
 constexpr int fast_nreg(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 2; }
-constexpr int fast_cw(int kt, bool bias) { return fast_big(kt, bias) ? 15 : 3; }
+constexpr int fast_cw(int kt, bool bias) {
+  return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 11 : 15) : 3;
+}
 // minimum waves per SIMD the register allocation must allow
-constexpr int fast_waves_per_eu(int kt, bool bias) { return fast_big(kt, bias) ? 4 : 2; }
+constexpr int fast_waves_per_eu(int kt, bool bias) {
+  return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 3 : 4) : 2;
+}
 constexpr int kFastTableBytes = 1024;  // LDS copy of the 256-entry table
 
 // position of key kappa inside its 64-key block of the staged V^T rows:

@@ -685,9 +685,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   if (d == D && kt == KT && bias == B && var == V) return iqattn_fast<D, KT, B, V>;
 
 // every row of up to 256 keys (KT <= 16) for both head sizes and all three back
-// ends, except d = 64 with 14 to 16 key tiles for Shiftmax and LIS MFMA (their
-// 16-wave workgroups would spill registers) and with 16 for LIS VALU (its three
-// buffers and shift scratch would pass 160 KB of LDS): the generic kernel runs those;
+// ends;
 // windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); every
 // longer row up to 640 keys (except LIS MFMA at d = 64 past 608 keys)
 #define IQ_FAST_ALL_VAR(D, KT)                 \
@@ -712,8 +710,9 @@ KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   // (d = 64, LIS MFMA at 609-640 keys would spill registers: generic kernel)
   if (d == 64 && kt >= 39 && var == kFastLisMfma) return nullptr;
   IQ_FAST_SHORT13(64)
-  IQ_FAST_CASE(64, 14, false, kFastLisValu)
-  IQ_FAST_CASE(64, 15, false, kFastLisValu)
+  IQ_FAST_ALL_VAR(64, 14)
+  IQ_FAST_ALL_VAR(64, 15)
+  IQ_FAST_ALL_VAR(64, 16)
   IQ_FAST_SHORT13(32)
   IQ_FAST_ALL_VAR(32, 14)
   IQ_FAST_ALL_VAR(32, 15)
