@@ -686,8 +686,9 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 
 // every row of up to 256 keys (KT <= 16) for both head sizes and all three back
 // ends;
-// windowed bias for windows of 7 x 7 (N = 49) and 12 x 12 (N = 144); every
-// longer row up to 640 keys (except LIS MFMA at d = 64 past 608 keys)
+// Shiftmax with the windowed bias for every window up to 25 x 25 (N = w^2
+// keys: every tile count up to 16, then those of w = 17..25); every longer row
+// up to 640 keys (except LIS MFMA at d = 64 past 608)
 #define IQ_FAST_ALL_VAR(D, KT)                 \
   IQ_FAST_CASE(D, KT, false, kFastShiftmax) \
   IQ_FAST_CASE(D, KT, false, kFastLisValu)  \
@@ -706,6 +707,14 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   IQ_FAST_ALL_VAR(D, 33) IQ_FAST_ALL_VAR(D, 34) IQ_FAST_ALL_VAR(D, 35) IQ_FAST_ALL_VAR(D, 36)  \
   IQ_FAST_ALL_VAR(D, 37) IQ_FAST_ALL_VAR(D, 38) IQ_FAST_ALL_VAR(D, 39) IQ_FAST_ALL_VAR(D, 40)
 
+#define IQ_FAST_B(D, KT) IQ_FAST_CASE(D, KT, true, kFastShiftmax)
+#define IQ_FAST_BIAS(D)                                                                     \
+  IQ_FAST_B(D, 1) IQ_FAST_B(D, 2) IQ_FAST_B(D, 3) IQ_FAST_B(D, 4) IQ_FAST_B(D, 5)               \
+  IQ_FAST_B(D, 6) IQ_FAST_B(D, 7) IQ_FAST_B(D, 8) IQ_FAST_B(D, 9) IQ_FAST_B(D, 10)              \
+  IQ_FAST_B(D, 11) IQ_FAST_B(D, 12) IQ_FAST_B(D, 13) IQ_FAST_B(D, 14) IQ_FAST_B(D, 15)          \
+  IQ_FAST_B(D, 16) IQ_FAST_B(D, 19) IQ_FAST_B(D, 21) IQ_FAST_B(D, 23) IQ_FAST_B(D, 25)         \
+  IQ_FAST_B(D, 28) IQ_FAST_B(D, 31) IQ_FAST_B(D, 34) IQ_FAST_B(D, 36) IQ_FAST_B(D, 40)
+
 KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   // (d = 64, LIS MFMA at 609-640 keys would spill registers: generic kernel)
   if (d == 64 && kt >= 39 && var == kFastLisMfma) return nullptr;
@@ -717,10 +726,8 @@ KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   IQ_FAST_ALL_VAR(32, 14)
   IQ_FAST_ALL_VAR(32, 15)
   IQ_FAST_ALL_VAR(32, 16)
-  IQ_FAST_CASE(64, 4, true, kFastShiftmax)
-  IQ_FAST_CASE(32, 4, true, kFastShiftmax)
-  IQ_FAST_CASE(64, 9, true, kFastShiftmax)
-  IQ_FAST_CASE(32, 9, true, kFastShiftmax)
+  IQ_FAST_BIAS(64)
+  IQ_FAST_BIAS(32)
   IQ_FAST_LONG(64)
   IQ_FAST_LONG(32)
   return nullptr;
