@@ -708,6 +708,9 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   IQ_FAST_ALL_VAR(D, 37) IQ_FAST_ALL_VAR(D, 38) IQ_FAST_ALL_VAR(D, 39) IQ_FAST_ALL_VAR(D, 40)
 
 #define IQ_FAST_B(D, KT) IQ_FAST_CASE(D, KT, true, kFastShiftmax)
+// Log-Int-Softmax with the windowed bias (both engines): 7 x 7, 8 x 8 and 12 x 12 windows
+#define IQ_FAST_LB(D, KT) \
+  IQ_FAST_CASE(D, KT, true, kFastLisValu) IQ_FAST_CASE(D, KT, true, kFastLisMfma)
 #define IQ_FAST_BIAS(D)                                                                     \
   IQ_FAST_B(D, 1) IQ_FAST_B(D, 2) IQ_FAST_B(D, 3) IQ_FAST_B(D, 4) IQ_FAST_B(D, 5)               \
   IQ_FAST_B(D, 6) IQ_FAST_B(D, 7) IQ_FAST_B(D, 8) IQ_FAST_B(D, 9) IQ_FAST_B(D, 10)              \
@@ -728,6 +731,7 @@ KernelFn fast_kernel(int d, int kt, bool bias, int var) {
   IQ_FAST_ALL_VAR(32, 16)
   IQ_FAST_BIAS(64)
   IQ_FAST_BIAS(32)
+  IQ_FAST_LB(64, 4) IQ_FAST_LB(64, 9) IQ_FAST_LB(32, 4) IQ_FAST_LB(32, 9)
   IQ_FAST_LONG(64)
   IQ_FAST_LONG(32)
   return nullptr;

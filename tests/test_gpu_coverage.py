@@ -61,21 +61,23 @@ def test_every_tile_count(torch_dev, d, variant, engine):
 
 
 @pytest.mark.parametrize("d", [32, 64])
-def test_every_window_with_bias(torch_dev, d):
+@pytest.mark.parametrize("variant,engine", ENGINES)
+def test_every_window_with_bias(torch_dev, d, variant, engine):
     """Windowed attention with the relative-position bias for every window
-    w = 1..25 (N = w^2), byte-exact."""
+    w = 1..25 (N = w^2), byte-exact, Shiftmax and both LIS engines."""
     from integer_only_quantized_int8_amd.iqattn import IQAttn
     torch = torch_dev
     dev = torch.device("cuda:0")
     for win in range(1, 26):
-        w = W.make_workload(2, 2, win * win, d, seed=950 + win, window=win)
-        _say(f"[coverage] window {win} (N = {win * win}), d = {d}, bias")
-        att = IQAttn(w.q.shape, w.params)
+        w = W.make_workload(2, 2, win * win, d, seed=950 + win, window=win, variant=variant)
+        _say(f"[coverage] window {win} (N = {win * win}), d = {d}, bias, variant {variant}, "
+             f"engine {engine}")
+        att = IQAttn(w.q.shape, dict(w.params, lis_engine=engine))
         q, k, v = (torch.from_numpy(x).to(dev) for x in (w.q, w.k, w.v))
         out = torch.full_like(q, 99)
         att.forward(q, k, v, out)
         torch.cuda.synchronize()
         got = out.cpu().numpy().reshape(4, win * win, d)
         att.close()
-        ref = oracle.forward(w.q, w.k, w.v, w.params)
+        ref = oracle.forward(w.q, w.k, w.v, dict(w.params, lis_engine=engine))
         assert np.array_equal(got, ref), f"window {win}: {np.argwhere(got != ref)[:4].tolist()}"
