@@ -567,13 +567,17 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           v4i O0[FT], O1[FT];
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) O0[ft] = O1[ft] = v4i{0, 0, 0, 0};
+          // (at 609-640 keys the V^T operands of a step are read at its start:
+          // one step of read-ahead would not fit the registers)
+          constexpr bool VPF = KT < 39;
           v4i vcur[FT], vnxt[FT];
           uint32_t va[FT][2];
           vt_addr<FT>(vbase, vtr, va);
-          read_vt<FT>(va, 0, vcur);
+          if (VPF) read_vt<FT>(va, 0, vcur);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) read_vt<FT>(va, (ks + 1) * 64 * D, vnxt);
+            if (!VPF) read_vt<FT>(va, ks * 64 * D, vcur);
+            if (VPF && ks + 1 < KS) read_vt<FT>(va, (ks + 1) * 64 * D, vnxt);
             v4i plo, phi;
             if (ks * 4 + 3 < KT) {
               lis_planes16(S[ks * 4], S[ks * 4 + 1], S[ks * 4 + 2], S[ks * 4 + 3], 0xFFu, plo, phi);
@@ -593,8 +597,9 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
               O1[ft] = mfma64(vcur[ft], phi, O1[ft]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (VPF)
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
+              for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
           }
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft)
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 // ends;
 // Shiftmax with the windowed bias for every window up to 25 x 25 (N = w^2
 // keys: every tile count up to 16, then those of w = 17..25); every longer row
-// up to 640 keys (except LIS MFMA at d = 64 past 608)
+// up to 640 keys
 #define IQ_FAST_ALL_VAR(D, KT)                 \
   IQ_FAST_CASE(D, KT, false, kFastShiftmax) \
   IQ_FAST_CASE(D, KT, false, kFastLisValu)  \
@@ -719,8 +724,6 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   IQ_FAST_B(D, 28) IQ_FAST_B(D, 31) IQ_FAST_B(D, 34) IQ_FAST_B(D, 36) IQ_FAST_B(D, 40)
 
 KernelFn fast_kernel(int d, int kt, bool bias, int var) {
-  // (d = 64, LIS MFMA at 609-640 keys would spill registers: generic kernel)
-  if (d == 64 && kt >= 39 && var == kFastLisMfma) return nullptr;
   IQ_FAST_SHORT13(64)
   IQ_FAST_ALL_VAR(64, 14)
   IQ_FAST_ALL_VAR(64, 15)
