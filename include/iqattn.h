@@ -58,6 +58,8 @@ extern "C" {
 #define IQATTN_E_NULL        -5  /* a required pointer is NULL                     */
 #define IQATTN_E_ALIGN       -6  /* a tensor pointer is not 16-byte aligned        */
 #define IQATTN_E_DEVICE      -7  /* no usable gfx950 device is current             */
+#define IQATTN_E_INCOMPLETE  -8  /* a kernel's bounded wait gave up: some output
+                                    rows of a launch were not written          */
 
 #define IQATTN_SHIFTMAX 0
 #define IQATTN_LIS      1
@@ -78,7 +80,9 @@ extern "C" {
 #define IQATTN_OUT_HEADS  0
 #define IQATTN_OUT_TOKENS 1
 
-#define IQATTN_MAX_SEQ 640       /* largest N of the fused register-resident kernel */
+#define IQATTN_MAX_SEQ 1024      /* largest N (up to 640 keys the row stays in
+                                    registers; longer rows take three passes over
+                                    LDS-resident K)                                */
 
 /* Parameters of one attention shape.  All values are plain integers.
  * Ranges (checked by iqattn_create, which returns IQATTN_E_INVAL or
@@ -93,7 +97,9 @@ extern "C" {
  *   IQATTN_LIS_MFMA (ignored for Shiftmax);
  *   rel_bias == NULL and window == 0, or rel_bias != NULL, window >= 1,
  *   seq_len == window * window and |rel_bias[.]| <= 2^30;
- *   out_layout IQATTN_OUT_HEADS or IQATTN_OUT_TOKENS.                    */
+ *   out_layout IQATTN_OUT_HEADS or IQATTN_OUT_TOKENS; for OUT_TOKENS
+ *   heads * seq_len * head_dim <= 2^31 - 1 (one head's output rows are
+ *   addressed with 32-bit offsets).                                       */
 typedef struct iqattn_params {
   int32_t batch, heads, seq_len, head_dim;
   int32_t qk_b, qk_c;        /* dyadic pair of Q.K^T -> int8 logits            */
@@ -114,8 +120,8 @@ typedef struct iqattn_params {
 typedef struct iqattn_ctx iqattn_ctx;
 
 /* Validate *p, then, on the current HIP device, allocate and fill the
- * context's device constants (exponential table, expanded bias) and pick the
- * kernel.  Synchronous.  On success *out owns a context that the caller frees
+ * context's device constants (exponential table, expanded bias) and its
+ * status word (see iqattn_check), and pick the kernel.  Synchronous.  On success *out owns a context that the caller frees
  * with iqattn_destroy; on error *out is set to NULL and nothing leaks.
  * Parameter checks happen before any HIP call.                              */
 int iqattn_create(const iqattn_params* p, iqattn_ctx** out);
@@ -131,6 +137,24 @@ int iqattn_create(const iqattn_params* p, iqattn_ctx** out);
  * undefined after an error.  A context may be used by several streams at once. */
 int iqattn_forward(iqattn_ctx* ctx, const int8_t* q, const int8_t* k,
                    const int8_t* v, int8_t* out, void* hip_stream);
+
+/* Completion check of the launches enqueued so far.  The kernels' work
+ * queues wait for data with bounded polls; a wave whose poll gives up (only
+ * a broken invariant or a test's spin limit can cause it) leaves its output
+ * rows unwritten and records the event in a status word owned by the context
+ * (set with a device atomic).  iqattn_check synchronises `hip_stream`, reads
+ * and clears that word, and returns IQATTN_OK, IQATTN_E_INCOMPLETE (some
+ * output of a launch since the last check is missing) or IQATTN_E_LAUNCH.
+ * The word is shared by every stream that uses the context.                 */
+int iqattn_check(iqattn_ctx* ctx, void* hip_stream);
+
+/* Diagnostic hook for tests of the failure path: every bounded poll of this
+ * context's later launches gives up after `polls` polls (>= 1; the default
+ * is 4194304, about 0.1 s per wait).  A small value makes waves give up
+ * while their data is still on the way: the kernels then exit normally and
+ * iqattn_check reports IQATTN_E_INCOMPLETE.  Returns IQATTN_E_INVAL for
+ * polls < 1.                                                                  */
+int iqattn_set_spin_limit(iqattn_ctx* ctx, int32_t polls);
 
 /* Free the context's device memory.  NULL is accepted (returns 0).  The
  * caller must make sure no forward using ctx is still running.              */

@@ -59,7 +59,8 @@ typedef struct iqlinear_params {
 typedef struct iqlinear_ctx iqlinear_ctx;
 
 /* Validate *p and pick the kernel for the current HIP device.  Synchronous;
- * allocates only the host-side context.  *out is NULL on error.              */
+ * allocates the context and its 4-byte device status word (see
+ * iqlinear_check).  *out is NULL on error.                                   */
 int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out);
 
 /* Enqueue Y = requant(X W^T) on `hip_stream` (a hipStream_t; NULL = null
@@ -70,6 +71,19 @@ int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out);
  * pointers, IQATTN_E_LAUNCH when the launch fails.                          */
 int iqlinear_forward(iqlinear_ctx* ctx, const int8_t* x, const int8_t* w, int8_t* out0,
                      int8_t* out1, int8_t* out2, void* hip_stream);
+
+/* Completion check of the launches enqueued so far: the pipelined kernel's
+ * waves wait for their operand stages with bounded polls, and a wave whose
+ * poll gives up leaves its output tiles unwritten and sets a bit in the
+ * context's status word (a device atomic).  Synchronises `hip_stream`, reads
+ * and clears the word; returns IQATTN_OK, IQATTN_E_INCOMPLETE or
+ * IQATTN_E_LAUNCH.                                                           */
+int iqlinear_check(iqlinear_ctx* ctx, void* hip_stream);
+
+/* Diagnostic hook for tests of the failure path: every bounded poll of later
+ * launches gives up after `polls` polls (>= 1; default 4194304).  Returns
+ * IQATTN_E_INVAL for polls < 1.                                              */
+int iqlinear_set_spin_limit(iqlinear_ctx* ctx, int32_t polls);
 
 /* Free the context (NULL accepted).                                          */
 int iqlinear_destroy(iqlinear_ctx* ctx);

@@ -72,6 +72,11 @@ int validate(const iqattn_params* p) {
     if (p->lis_engine != IQATTN_LIS_VALU && p->lis_engine != IQATTN_LIS_MFMA) return IQATTN_E_INVAL;
   }
   if (p->out_layout != IQATTN_OUT_HEADS && p->out_layout != IQATTN_OUT_TOKENS) return IQATTN_E_INVAL;
+  // token-major output: one head's rows span (N - 1) H d + d bytes, addressed
+  // with 32-bit offsets in the kernels
+  if (p->out_layout == IQATTN_OUT_TOKENS &&
+      (int64_t)p->heads * p->seq_len * p->head_dim > INT32_MAX)
+    return IQATTN_E_SHAPE;
   if (p->rel_bias == NULL) {
     if (p->window != 0) return IQATTN_E_INVAL;
   } else {
@@ -96,10 +101,12 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   if (!fast_kernel(p->head_dim, kt, p->rel_bias != NULL, var)) return false;
   // requantisation: floor(b x / 2^c) = mulhi32(x, b << (32 - c)) for
   // b << (32 - c) < 2^31; padded keys carry mask_s = -(smax + 1), below every
-  // real accumulator; every raw logit then fits the 24-bit v_mad_i32_i24
+  // real accumulator; every raw logit then fits the 24-bit v_mad_i32_i24.
+  // Inputs are any int8 values: |q_t k_t| <= 128 * 128 (both -128), so
+  // |acc| <= d * 128 * 128 + bias_max.
   if (p->qk_c > 32 || p->qk_c < 1) return false;
   if (((int64_t)p->qk_b << (32 - p->qk_c)) >= ((int64_t)1 << 31)) return false;
-  const int64_t smax = (int64_t)p->head_dim * 127 * 127 + bias_max;
+  const int64_t smax = (int64_t)p->head_dim * 128 * 128 + bias_max;
   if ((((smax + 1) * p->qk_b) >> p->qk_c) >= (1 << 22)) return false;
   // IntDiv product: floor(e f / 2^sh) = mulhi32(e 2^ea, f 2^fb), ea + fb = 32 - sh,
   // sh = M - (k_out - 1) (Shiftmax) or M - F (LIS); the table holds e 2^ea
@@ -150,11 +157,16 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
 
 }  // namespace
 
+// Polls of a bounded work-queue wait (each followed by s_sleep 1, about 64
+// clocks) before a wave gives up; only a broken invariant could reach it.
+constexpr int32_t kDefaultSpinLimit = 1 << 22;
+
 struct iqattn_ctx {
   iqattn_params p;
   int device;
   uint32_t* exp_tab;
   int32_t* bias;
+  uint32_t* status;  // bits of bounded waits that gave up (iqattn_check)
   KernelFn fn;
   size_t lds_bytes;
   DevParams dp;
@@ -197,6 +209,11 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   if (hipMalloc((void**)&c->exp_tab, 256 * sizeof(uint32_t)) != hipSuccess) {
     free(c);
     return IQATTN_E_ALLOC;
+  }
+  if (hipMalloc((void**)&c->status, sizeof(uint32_t)) != hipSuccess) { rc = IQATTN_E_ALLOC; goto fail; }
+  if ((e = hipMemset(c->status, 0, sizeof(uint32_t))) != hipSuccess) {
+    rc = set_hip_error(e, "status word");
+    goto fail;
   }
   hipLaunchKernelGGL(iqattn_build_exp, dim3(1), dim3(256), 0, 0, c->exp_tab, p->i0,
                      p->exp_frac_bits, c->fast ? c->dp.e_shift : 0);
@@ -247,6 +264,12 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
       c->fn = fast_kernel(D, KT, bias, var);
       c->lds_bytes = used > reach ? used : reach;
       c->block = (int)(64 * (cw + 1));
+    } else if (KT > 40) {
+      // rows of 641..1024 keys: three passes over LDS-resident K, every back end
+      const int var = fast_variant(p);
+      c->fn = long_kernel(D, var, p->rel_bias != NULL);
+      c->block = long_threads();
+      c->lds_bytes = long_lds_bytes(D, N, var);
     } else {
       vbytes = (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
       c->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);
@@ -268,6 +291,8 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   }
   c->dp.exp_tab = c->exp_tab;
   c->dp.bias = c->bias;
+  c->dp.status = c->status;
+  c->dp.spin_limit = kDefaultSpinLimit;
   c->dp.heads = p->heads;
   c->dp.n = N;
   c->dp.out_tok = p->out_layout == IQATTN_OUT_TOKENS;
@@ -306,6 +331,7 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
 fail:
   if (c->exp_tab) (void)hipFree(c->exp_tab);
   if (c->bias) (void)hipFree(c->bias);
+  if (c->status) (void)hipFree(c->status);
   free(c);
   return rc;
 }
@@ -328,6 +354,27 @@ extern "C" int iqattn_forward(iqattn_ctx* c, const int8_t* q, const int8_t* k, c
   return IQATTN_OK;
 }
 
+extern "C" int iqattn_check(iqattn_ctx* c, void* hip_stream) {
+  if (!c) return IQATTN_E_NULL;
+  hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
+  if (e != hipSuccess) return set_hip_error(e, "iqattn_check synchronize");
+  uint32_t word = 0;
+  if ((e = hipMemcpy(&word, c->status, sizeof(word), hipMemcpyDeviceToHost)) != hipSuccess)
+    return set_hip_error(e, "iqattn_check read");
+  if (word == 0) return IQATTN_OK;
+  const uint32_t zero = 0;
+  if ((e = hipMemcpy(c->status, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+    return set_hip_error(e, "iqattn_check clear");
+  return IQATTN_E_INCOMPLETE;
+}
+
+extern "C" int iqattn_set_spin_limit(iqattn_ctx* c, int32_t polls) {
+  if (!c) return IQATTN_E_NULL;
+  if (polls < 1) return IQATTN_E_INVAL;
+  c->dp.spin_limit = polls;
+  return IQATTN_OK;
+}
+
 extern "C" int iqattn_destroy(iqattn_ctx* c) {
   if (!c) return IQATTN_OK;
   int dev = 0;
@@ -335,6 +382,7 @@ extern "C" int iqattn_destroy(iqattn_ctx* c) {
   (void)hipSetDevice(c->device);
   if (c->exp_tab) (void)hipFree(c->exp_tab);
   if (c->bias) (void)hipFree(c->bias);
+  if (c->status) (void)hipFree(c->status);
   (void)hipSetDevice(dev);
   free(c);
   return IQATTN_OK;
@@ -350,6 +398,7 @@ extern "C" const char* iqattn_strerror(int code) {
     case IQATTN_E_NULL: return "required pointer is NULL";
     case IQATTN_E_ALIGN: return "tensor pointer not 16-byte aligned";
     case IQATTN_E_DEVICE: return "no usable gfx950 device";
+    case IQATTN_E_INCOMPLETE: return "a bounded wait in the kernel gave up: output incomplete";
     default: return "unknown error code";
   }
 }

@@ -47,7 +47,21 @@ struct DevParams {
   int32_t e0, e0_pow2;           // e(0) and whether it divides 2^M
   int32_t pv_fast, pv_bm;        // output requantisation as mulhi(o, pv_bm)
   int32_t p_u24;                 // Shiftmax: e << e_shift and F below 2^24 (p16_pack24)
+  uint32_t* status;              // context status word: kStatus* bits of waits that gave up
+  int32_t spin_limit;            // polls of a bounded wait before it gives up
 };
+
+// Bits of the status word.  A wave whose bounded wait gives up sets its bit
+// (one device atomic from lane 0, a vector memory operation) and exits; the
+// output rows it would have written stay unwritten.
+constexpr uint32_t kStatusLoader = 1u;    // loader wave: a buffer was never released
+constexpr uint32_t kStatusKQ = 2u;        // compute wave: K and Q never arrived
+constexpr uint32_t kStatusV = 4u;         // compute wave: V never arrived
+
+__device__ __forceinline__ void report_giveup(const DevParams& p, uint32_t bit) {
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(p.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 typedef void (*KernelFn)(DevParams);
 
@@ -282,6 +296,59 @@ __device__ __forceinline__ int32_t ilog2r_dev(uint32_t x) {
   return k + nb;
 }
 
+// ---------------------------------------------------------------- LDS layouts of K and V
+// XOR swizzles of the 16-byte chunk index of an LDS row.  K (b128 / b64
+// operand reads of 16 rows): d = 64 by (row >> 1) & 3, d = 32 by (row >> 3) & 1.
+// V (transpose reads of keys 16 tt + 4 g + r): d = 64 by bits 2 and 4 of the
+// key, d = 32 by bit 4; both spread a half-wave over distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 64 ? (row >> 1) & 3 : (row >> 3) & 1;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 64 ? (((row >> 2) & 1) | ((row >> 3) & 2)) : (row >> 4) & 1;
+}
+
+// V^T operands by transpose reads: two ds_read_b64_tr_b8 per 16-feature tile
+// at the lane offsets vtr[0], vtr[1], the feature tile entering as an XOR of
+// the 16-byte chunk index.  vt_addr forms a tile's eight lane addresses once;
+// read_vt adds the 64-key step's byte offset, a constant the reads carry in
+// their offset field.
+template <int FT>
+__device__ __forceinline__ void vt_addr(uint32_t vb, const int (&vtr)[2], uint32_t (&va)[FT][2]) {
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    va[ft][0] = vb + (uint32_t)(vtr[0] ^ (ft << 4));
+    va[ft][1] = vb + (uint32_t)(vtr[1] ^ (ft << 4));
+  }
+}
+template <int FT>
+__device__ __forceinline__ void read_vt(const uint32_t (&va)[FT][2], uint32_t off, v4i (&vop)[FT]) {
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][0] + off));
+    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][1] + off));
+    vop[ft] = v4i{r0[0], r0[1], r1[0], r1[1]};
+  }
+}
+
+// LIS bit-plane operand bytes of four shifts (w in the low four bits of each
+// word): plane 0 gets -2^w for w < 8, plane 1 gets -2^(w-8) for w >= 8 (as
+// int8 bytes 0xFF << l).
+__device__ __forceinline__ void lis_planes(const v4i& w, int32_t& lo, int32_t& hi) {
+  uint32_t y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {  // 16-bit (plane 1 byte, plane 0 byte)
+    const uint32_t l = (uint32_t)w[r] & 15u;
+    y[r] = (0xFFu << l) & (0xFFu << (l & 8));
+  }
+  const uint32_t t01 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
+  const uint32_t t23 = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
+  lo = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
+  hi = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
+}
+
 // ---------------------------------------------------------------- MFMA
 template <int D>
 struct Mfma;
@@ -313,5 +380,9 @@ int set_hip_error(hipError_t e, const char* what);
 // host-side selectors, one per translation unit
 KernelFn generic_kernel(int d, int ktm, int variant, bool bias);
 KernelFn fast_kernel(int d, int kt, bool bias, int var);  // null if not instantiated
+// rows of 641..1024 keys (three passes over LDS-resident K); var is a kFast* back end
+KernelFn long_kernel(int d, int var, bool bias);
+size_t long_lds_bytes(int d, int n, int var);
+int long_threads();
 
 }  // namespace iqattn

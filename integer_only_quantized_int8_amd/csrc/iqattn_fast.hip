@@ -44,18 +44,6 @@
 namespace iqattn {
 namespace {
 
-// XOR swizzles of the 16-byte chunk index of an LDS row.  K (b128 / b64
-// operand reads of 16 rows): d = 64 by (row >> 1) & 3, d = 32 by (row >> 3) & 1.
-// V (transpose reads of keys 16 tt + 4 g + r): d = 64 by bits 2 and 4 of the
-// key, d = 32 by bit 4; both spread a half-wave over distinct banks.
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  return D == 64 ? (row >> 1) & 3 : (row >> 3) & 1;
-}
-template <int D>
-__device__ __forceinline__ int vswz(int row) {
-  return D == 64 ? (((row >> 2) & 1) | ((row >> 3) & 2)) : (row >> 4) & 1;
-}
 
 // LIS shift w = F - code of the probability Ph = (f e) >> (M - F).  Ph <= 2^F
 // (e is at most the row sum s and f = floor(2^M / s)), so w = ilog2r(max(Ph, 1))
@@ -81,21 +69,6 @@ __device__ __forceinline__ int32_t shl_add(int32_t v, int32_t w, int32_t o) {
   return r;
 }
 
-// LIS bit-plane operand bytes of four shifts (w in the low four bits of each
-// word): plane 0 gets -2^w for w < 8, plane 1 gets -2^(w-8) for w >= 8 (as
-// int8 bytes 0xFF << l).
-__device__ __forceinline__ void lis_planes(const v4i& w, int32_t& lo, int32_t& hi) {
-  uint32_t y[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {  // 16-bit (plane 1 byte, plane 0 byte)
-    const uint32_t l = (uint32_t)w[r] & 15u;
-    y[r] = (0xFFu << l) & (0xFFu << (l & 8));
-  }
-  const uint32_t t01 = __builtin_amdgcn_perm(y[1], y[0], 0x05010400u);
-  const uint32_t t23 = __builtin_amdgcn_perm(y[3], y[2], 0x05010400u);
-  lo = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x05040100u);
-  hi = (int32_t)__builtin_amdgcn_perm(t23, t01, 0x07060302u);
-}
 
 // The two bit-plane operand words of sixteen LIS shifts at once (four 16-key
 // tiles of four keys).  Each input holds w (mod 16) in byte 0 and w + 8 (mod
@@ -217,28 +190,6 @@ __device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t v
 // s_waitcnt immediate for vmcnt(n), other counters untouched (n < 64)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// V^T operands by transpose reads: two ds_read_b64_tr_b8 per 16-feature tile
-// at the lane offsets vtr[0], vtr[1], the feature tile entering as an XOR of
-// the 16-byte chunk index.  vt_addr forms a tile's eight lane addresses once;
-// read_vt adds the 64-key step's byte offset, a constant the reads carry in
-// their offset field.
-template <int FT>
-__device__ __forceinline__ void vt_addr(uint32_t vb, const int (&vtr)[2], uint32_t (&va)[FT][2]) {
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    va[ft][0] = vb + (uint32_t)(vtr[0] ^ (ft << 4));
-    va[ft][1] = vb + (uint32_t)(vtr[1] ^ (ft << 4));
-  }
-}
-template <int FT>
-__device__ __forceinline__ void read_vt(const uint32_t (&va)[FT][2], uint32_t off, v4i (&vop)[FT]) {
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][0] + off));
-    const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(uintptr_t)(va[ft][1] + off));
-    vop[ft] = v4i{r0[0], r0[1], r1[0], r1[1]};
-  }
-}
 
 // Output requantisation and store of a lane's 4 x FT int32 sums (features
 // 16 ft + 4 g + r of one query, at byte offset dst + 16 ft of the head).
@@ -265,10 +216,6 @@ __device__ __forceinline__ void store_out(const DevParams& p, const v4i (&O)[FT]
           ores, dst + ft * 16, 0, 0);
   }
 }
-
-// Polls of a work-queue word (each followed by s_sleep 1, about 64 clocks)
-// before a wave gives up; only a broken invariant could ever reach it.
-constexpr int kSpinLimit = 1 << 22;
 
 template <int D, int KT, bool BIAS, int VAR>
 __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT, BIAS)) void iqattn_fast(
@@ -326,10 +273,15 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       const int b = j % NBUF;
       if (j >= NBUF) {
         const int tprev = decode_item<KT>(p, (int)blockIdx.x + (j - NBUF) * G).T;
+        // (bounded: p.spin_limit polls of about 64 clocks each; only a broken
+        // invariant, or a test's tiny limit, makes a wave give up)
         int spins = 0;
         while (__hip_atomic_load(&ctl_done[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
                tprev) {
-          if (++spins > kSpinLimit) return;
+          if (++spins > p.spin_limit) {
+            report_giveup(p, kStatusLoader);
+            return;
+          }
           __builtin_amdgcn_s_sleep(1);
         }
       }
@@ -394,7 +346,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
     if (have < jw) {
       int spins = 0;
       while (__hip_atomic_load(&ctl_ready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != jw) {
-        if (++spins > kSpinLimit) return;
+        if (++spins > p.spin_limit) {
+          report_giveup(p, kStatusKQ);
+          return;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
       have = jw;
@@ -510,7 +465,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       if (havev < jw) {
         int spins = 0;
         while (__hip_atomic_load(&ctl_vready[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != jw) {
-          if (++spins > kSpinLimit) return;
+          if (++spins > p.spin_limit) {
+            report_giveup(p, kStatusV);
+            return;
+          }
           __builtin_amdgcn_s_sleep(1);
         }
         havev = jw;

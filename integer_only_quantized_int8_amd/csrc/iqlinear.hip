@@ -50,7 +50,14 @@ struct LinParams {
   // (Granlund and Montgomery's division by an invariant integer)
   uint32_t seq_magic;
   int32_t seq_shift;
+  uint32_t* status;    // context status word: bit 0 loader, bit 1 compute wave gave up
+  int32_t spin_limit;  // polls of a bounded wait before it gives up
 };
+
+__device__ __forceinline__ void lin_giveup(const LinParams& p, uint32_t bit) {
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(p.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <typename T>
 __device__ __forceinline__ T pick3(int which, T a0, T a1, T a2) {
@@ -248,7 +255,6 @@ constexpr int kPipeKB = 128;  // k bytes of a row per stage: whole cache lines p
 constexpr int kPipeNS = 4;
 constexpr int kPipeLag = 2;
 constexpr int kPipeNL = 4;
-constexpr int kPipeSpin = 1 << 22;
 constexpr int kPipeThreads = 64 * (4 + kPipeNL);
 
 constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -315,7 +321,11 @@ __global__ __launch_bounds__(kPipeThreads) void iqlinear_pipe(LinParams p) {
           const int need = 4 * (s / NS);
           int spins = 0;
           while (__hip_atomic_load(&done[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
-            if (++spins > kPipeSpin) return;
+            if (++spins > p.spin_limit) {
+              lin_giveup(p, 1u);
+              __builtin_amdgcn_s_waitcnt(0);  // no direct loads left in flight
+              return;
+            }
             __builtin_amdgcn_s_sleep(1);
           }
         }
@@ -356,7 +366,10 @@ __global__ __launch_bounds__(kPipeThreads) void iqlinear_pipe(LinParams p) {
     const int need = NL * (step / NS + 1);
     int spins = 0;
     while (__hip_atomic_load(&ready[step % NS], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
-      if (++spins > kPipeSpin) return false;
+      if (++spins > p.spin_limit) {
+        lin_giveup(p, 2u);
+        return false;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     return true;
@@ -450,6 +463,7 @@ struct iqlinear_ctx {
   LinParams lp;
   int device;
   unsigned grid;  // persistent grid of the pipelined kernel
+  uint32_t* status;
 };
 
 extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
@@ -540,6 +554,17 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
       return IQATTN_E_DEVICE;
     }
   }
+  if (hipMalloc((void**)&c->status, sizeof(uint32_t)) != hipSuccess) {
+    free(c);
+    return IQATTN_E_ALLOC;
+  }
+  if (hipMemset(c->status, 0, sizeof(uint32_t)) != hipSuccess) {
+    (void)hipFree(c->status);
+    free(c);
+    return IQATTN_E_DEVICE;
+  }
+  lp.status = c->status;
+  lp.spin_limit = 1 << 22;  // polls of about 64 clocks: only a broken invariant gives up
   *out = c;
   return IQATTN_OK;
 }
@@ -567,7 +592,36 @@ extern "C" int iqlinear_forward(iqlinear_ctx* c, const int8_t* x, const int8_t* 
   return IQATTN_OK;
 }
 
+extern "C" int iqlinear_check(iqlinear_ctx* c, void* hip_stream) {
+  if (!c) return IQATTN_E_NULL;
+  hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
+  if (e != hipSuccess) return set_hip_error(e, "iqlinear_check synchronize");
+  uint32_t word = 0;
+  if ((e = hipMemcpy(&word, c->status, sizeof(word), hipMemcpyDeviceToHost)) != hipSuccess)
+    return set_hip_error(e, "iqlinear_check read");
+  if (word == 0) return IQATTN_OK;
+  const uint32_t zero = 0;
+  if ((e = hipMemcpy(c->status, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+    return set_hip_error(e, "iqlinear_check clear");
+  return IQATTN_E_INCOMPLETE;
+}
+
+extern "C" int iqlinear_set_spin_limit(iqlinear_ctx* c, int32_t polls) {
+  if (!c) return IQATTN_E_NULL;
+  if (polls < 1) return IQATTN_E_INVAL;
+  c->lp.spin_limit = polls;
+  return IQATTN_OK;
+}
+
 extern "C" int iqlinear_destroy(iqlinear_ctx* c) {
+  if (!c) return IQATTN_OK;
+  if (c->status) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipSetDevice(c->device);
+    (void)hipFree(c->status);
+    (void)hipSetDevice(dev);
+  }
   free(c);
   return IQATTN_OK;
 }

@@ -25,18 +25,21 @@ IQATTN_E_LAUNCH = -4
 IQATTN_E_NULL = -5
 IQATTN_E_ALIGN = -6
 IQATTN_E_DEVICE = -7
+IQATTN_E_INCOMPLETE = -8
 IQATTN_SHIFTMAX = 0
 IQATTN_LIS = 1
 IQATTN_OUT_HEADS = 0
 IQATTN_OUT_TOKENS = 1
 IQATTN_LIS_VALU = 0
 IQATTN_LIS_MFMA = 1
-IQATTN_MAX_SEQ = 640
+IQATTN_MAX_SEQ = 1024
 IQLINEAR_PLAIN = 0
 IQLINEAR_QKV_HEADS = 1
 
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
-            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy",
+            "iqattn_check", "iqattn_set_spin_limit",
+            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy", "iqlinear_check",
+            "iqlinear_set_spin_limit",
             "iqgelu_create", "iqgelu_forward", "iqgelu_destroy",
             "iqlayernorm_create", "iqlayernorm_forward", "iqlayernorm_destroy",
             "iqlinattn_create", "iqlinattn_forward", "iqlinattn_destroy")
@@ -96,12 +99,20 @@ def load_library():
         lib.iqattn_destroy.restype = C.c_int
         lib.iqattn_strerror.argtypes = [C.c_int]
         lib.iqattn_strerror.restype = C.c_char_p
+        lib.iqattn_check.argtypes = [C.c_void_p, C.c_void_p]
+        lib.iqattn_check.restype = C.c_int
+        lib.iqattn_set_spin_limit.argtypes = [C.c_void_p, C.c_int32]
+        lib.iqattn_set_spin_limit.restype = C.c_int
         lib.iqlinear_create.argtypes = [C.POINTER(iqlinear_params), C.POINTER(C.c_void_p)]
         lib.iqlinear_create.restype = C.c_int
         lib.iqlinear_forward.argtypes = [C.c_void_p] * 7
         lib.iqlinear_forward.restype = C.c_int
         lib.iqlinear_destroy.argtypes = [C.c_void_p]
         lib.iqlinear_destroy.restype = C.c_int
+        lib.iqlinear_check.argtypes = [C.c_void_p, C.c_void_p]
+        lib.iqlinear_check.restype = C.c_int
+        lib.iqlinear_set_spin_limit.argtypes = [C.c_void_p, C.c_int32]
+        lib.iqlinear_set_spin_limit.restype = C.c_int
         lib.iqgelu_create.argtypes = [C.POINTER(iqgelu_params), C.POINTER(C.c_void_p)]
         lib.iqgelu_create.restype = C.c_int
         lib.iqgelu_forward.argtypes = [C.c_void_p] * 4
@@ -177,6 +188,21 @@ def iqattn_destroy(ctx: Optional[int]) -> None:
         raise IQAttnError(rc, "iqattn_destroy")
 
 
+def iqattn_check(ctx: int, stream=None) -> int:
+    """Synchronise `stream` and return the context's completion status
+    (IQATTN_OK or IQATTN_E_INCOMPLETE); raises on other errors."""
+    rc = load_library().iqattn_check(C.c_void_p(ctx), C.c_void_p(_stream_handle(stream)))
+    if rc not in (IQATTN_OK, IQATTN_E_INCOMPLETE):
+        raise IQAttnError(rc, "iqattn_check")
+    return rc
+
+
+def iqattn_set_spin_limit(ctx: int, polls: int) -> None:
+    rc = load_library().iqattn_set_spin_limit(C.c_void_p(ctx), int(polls))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqattn_set_spin_limit")
+
+
 class IQAttn:
     """Owns one context for a fixed shape and parameter set."""
 
@@ -207,6 +233,11 @@ class IQAttn:
         return out
 
     __call__ = forward
+
+    def check(self, stream=None) -> int:
+        """IQATTN_OK, or IQATTN_E_INCOMPLETE if a launch since the last check
+        left output rows unwritten (synchronises the stream)."""
+        return iqattn_check(self.ctx, stream)
 
     def close(self):
         if self.ctx:
@@ -259,6 +290,19 @@ def iqlinear_destroy(ctx: Optional[int]) -> None:
         raise IQAttnError(rc, "iqlinear_destroy")
 
 
+def iqlinear_check(ctx: int, stream=None) -> int:
+    rc = load_library().iqlinear_check(C.c_void_p(ctx), C.c_void_p(_stream_handle(stream)))
+    if rc not in (IQATTN_OK, IQATTN_E_INCOMPLETE):
+        raise IQAttnError(rc, "iqlinear_check")
+    return rc
+
+
+def iqlinear_set_spin_limit(ctx: int, polls: int) -> None:
+    rc = load_library().iqlinear_set_spin_limit(C.c_void_p(ctx), int(polls))
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqlinear_set_spin_limit")
+
+
 class IQLinear:
     """Owns one linear-layer context: x [rows, in] int8, w [out, in] int8."""
 
@@ -286,6 +330,11 @@ class IQLinear:
         return out
 
     __call__ = forward
+
+    def check(self, stream=None) -> int:
+        """IQATTN_OK, or IQATTN_E_INCOMPLETE if a launch since the last check
+        left output tiles unwritten (synchronises the stream)."""
+        return iqlinear_check(self.ctx, stream)
 
     def close(self):
         if self.ctx:

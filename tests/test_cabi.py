@@ -43,7 +43,8 @@ def test_header_constants_match_binding():
     for name in ("IQATTN_OK", "IQATTN_E_INVAL", "IQATTN_E_SHAPE", "IQATTN_E_ALLOC",
                  "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
                  "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_LIS_VALU", "IQATTN_LIS_MFMA",
-                 "IQATTN_OUT_HEADS", "IQATTN_OUT_TOKENS", "IQATTN_MAX_SEQ"):
+                 "IQATTN_OUT_HEADS", "IQATTN_OUT_TOKENS", "IQATTN_MAX_SEQ",
+                 "IQATTN_E_INCOMPLETE"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(IQ, name), name
     text = open(os.path.join(ROOT, "include", "iqlinear.h")).read()
@@ -64,7 +65,8 @@ def _create_rc(lib, shape, **over):
 
 @pytest.mark.parametrize("shape,over,code", [
     ((1, 1, 0, 64), {}, IQ.IQATTN_E_SHAPE),
-    ((1, 1, 641, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 1, 1025, 64), {}, IQ.IQATTN_E_SHAPE),
+    ((1, 40000, 1024, 64), {"out_layout": 1}, IQ.IQATTN_E_SHAPE),
     ((1, 1, 16, 48), {}, IQ.IQATTN_E_SHAPE),
     ((-1, 1, 16, 64), {}, IQ.IQATTN_E_SHAPE),
     ((1, 0, 16, 64), {}, IQ.IQATTN_E_SHAPE),
@@ -98,10 +100,12 @@ def test_null_pointers_and_destroy_null(lib):
     assert lib.iqattn_create(C.byref(p), None) == IQ.IQATTN_E_NULL
     assert lib.iqattn_destroy(None) == IQ.IQATTN_OK
     assert lib.iqattn_forward(None, None, None, None, None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqattn_check(None, None) == IQ.IQATTN_E_NULL
+    assert lib.iqattn_set_spin_limit(None, 1) == IQ.IQATTN_E_NULL
 
 
 def test_strerror_texts(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
         s = IQ.iqattn_strerror(code)
         assert isinstance(s, str) and s
 

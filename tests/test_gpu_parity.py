@@ -39,6 +39,8 @@ def run_gpu(torch, w, params=None, stream=None):
     att.forward(q, k, v, out, stream=stream)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
+    from integer_only_quantized_int8_amd.iqattn import IQATTN_OK
+    assert att.check(stream) == IQATTN_OK, "a bounded wait gave up"
     att.close()
     return res
 
@@ -85,12 +87,9 @@ def test_headline_config_all_heads(torch_dev):
     check(torch_dev, w, label="shape 2 seed 1002 (all 1536 heads)")
 
 
-def test_lis_config_sampled_heads(torch_dev):
+def test_lis_config_all_heads(torch_dev):
     w = W.config_workload(4)
-    total = w.batch * w.heads
-    heads = sorted(set([0, 1, total - 1] + list(np.random.default_rng(0).choice(total, 9,
-                                                                            replace=False))))
-    check(torch_dev, w, heads=heads, label="shape 4 seed 1004 (sampled heads)")
+    check(torch_dev, w, label="shape 4 seed 1004 (all 512 heads, both P.V engines)")
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
@@ -105,10 +104,43 @@ def test_configs_other_seeds_reduced_batch(torch_dev, cfg, seed):
 @pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("d", [32, 64])
 @pytest.mark.parametrize("N", [1, 2, 15, 16, 17, 31, 33, 49, 63, 64, 65, 130, 197, 208, 209,
-                               400, 577, 640])
+                               400, 577, 640, 641, 768, 1000, 1024])
 def test_edge_shapes(torch_dev, N, d, variant):
     w = W.make_workload(2, 3, N, d, seed=N * 7 + d + variant, variant=variant)
     check(torch_dev, w, label=f"edge N={N} d={d}")
+
+
+@pytest.mark.parametrize("w,d", [(26, 64), (32, 32), (32, 64)])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_long_rows_with_window_bias(torch_dev, w, d, variant):
+    wl = W.make_workload(1, 2, w * w, d, seed=w * 3 + d + variant, variant=variant, window=w)
+    check(torch_dev, wl, label=f"long row with bias w={w} d={d}")
+
+
+@pytest.mark.parametrize("N,d,window", [(2, 64, 0), (37, 64, 0), (197, 64, 0), (25, 32, 5),
+                                        (49, 64, 7), (700, 64, 0)])
+@pytest.mark.parametrize("variant", [0, 1])
+def test_int8_extremes(torch_dev, N, d, window, variant):
+    """Inputs at both ends of int8 (-128 included, which the header accepts
+    although the workloads clip to +-127), a small requantisation scale and
+    i0 = 3, so that accumulators reach d * 128 * 128 in magnitude: padded keys
+    must still stay below every real key of the row."""
+    wl = W.make_workload(2, 2, N, d, seed=N + d + window + variant, variant=variant,
+                         window=window)
+    rng = np.random.default_rng(N * 7 + variant)
+    ext = np.array([-128, 127, -127, 0], dtype=np.int8)
+    for t in (wl.q, wl.k, wl.v):
+        t[:] = rng.choice(ext, size=t.shape, p=[0.45, 0.45, 0.05, 0.05])
+    wl.q[0, 0] = -128                       # rows whose every product is -128 * 127
+    wl.k[0, 0] = 127
+    params = dict(wl.params, qk_b=511, qk_c=22, i0=3)
+    if variant == 1:
+        params["pv_c"] = 28
+    check(torch_dev, wl, params=params, label=f"int8 extremes N={N} d={d} window={window}")
+    if N == 2:                              # Q = -128 and K = 127 everywhere
+        wl.q[:] = -128
+        wl.k[:] = 127
+        check(torch_dev, wl, params=params, label="Q=-128 K=127")
 
 
 def test_all_equal_logits(torch_dev):
