@@ -117,6 +117,8 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   if (sh < 0 || sh > 32 || p->intdiv_m > 30) return false;
   const int64_t np = (int64_t)kt * 16;
   if (np * e0 >= (1 << 24)) return false;           // exact float row sum
+  // the expanded bias is read through a buffer resource with 32-bit offsets
+  if (p->rel_bias && (int64_t)p->heads * np * np * 4 > INT32_MAX) return false;
   if (two_m / e0 > (1 << 22)) return false;         // reciprocal estimate within 1/2
   const bool pow2 = (e0 & (e0 - 1)) == 0 && e0 <= two_m;
   if (var == kFastShiftmax && e0 > ((int64_t)1 << sh)) return false;  // f - 1 clamp case
@@ -264,6 +266,14 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
       c->fn = fast_kernel(D, KT, bias, var);
       c->lds_bytes = used > reach ? used : reach;
       c->block = (int)(64 * (cw + 1));
+      // rows of 64 keys: the expanded bias of every head in LDS after the
+      // work-queue words, when it fits (the per-tile reads then leave global
+      // memory, where they also waited for the previous tile's stores)
+      const size_t bias_bytes = (size_t)p->heads * 64 * 64 * 4;
+      if (bias && KT == 4 && used + bias_bytes <= 160 * 1024) {
+        c->dp.bias_lds = 1;
+        c->lds_bytes = used + bias_bytes;
+      }
     } else if (KT > 40) {
       // rows of 641..1024 keys: three passes over LDS-resident K, every back end
       const int var = fast_variant(p);

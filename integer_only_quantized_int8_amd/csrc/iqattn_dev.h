@@ -47,6 +47,7 @@ struct DevParams {
   int32_t e0, e0_pow2;           // e(0) and whether it divides 2^M
   int32_t pv_fast, pv_bm;        // output requantisation as mulhi(o, pv_bm)
   int32_t p_u24;                 // Shiftmax: e << e_shift and F below 2^24 (p16_pack24)
+  int32_t bias_lds;              // windowed bias of 64-key rows staged in LDS (fast kernels)
   uint32_t* status;              // context status word: kStatus* bits of waits that gave up
   int32_t spin_limit;            // polls of a bounded wait before it gives up
 };
@@ -274,8 +275,11 @@ constexpr int fast_cw(int kt, bool bias) {
   return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 11 : 15) : 3;
 }
 // minimum waves per SIMD the register allocation must allow
+// (rows of up to 64 keys: 8 waves per SIMD, so that two 16-wave workgroups
+// share a CU; the bound keeps the scalar registers within what eight waves
+// per SIMD can hold)
 constexpr int fast_waves_per_eu(int kt, bool bias) {
-  return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 3 : 4) : 2;
+  return kt <= 4 ? 8 : (fast_big(kt, bias) ? (fast_mid(kt, bias) ? 3 : 4) : 2);
 }
 constexpr int kFastTableBytes = 1024;  // LDS copy of the 256-entry table
 

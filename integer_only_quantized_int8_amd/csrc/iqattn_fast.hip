@@ -156,26 +156,37 @@ __device__ __forceinline__ Item decode_item(const DevParams& p, int k) {
   return it;
 }
 
+// Key held by accumulator row 4 g + r of the last 16-key tile when its rows
+// are transposed: 4 r + g.
+__device__ __forceinline__ int kt_perm(int pos) { return ((pos & 3) << 2) | (pos >> 2); }
+
 // Direct loads of head u's K (and Q), then V (R / 1024 blocks each) into the
 // LDS regions at vbuf + R (and vbuf + 2R) and vbuf, issued by one wave.  Lane l of block i fills LDS bytes
 // [1024 i + 16 l, +16) = (row, chunk position cp) from source chunk
 // cp ^ swizzle(row).  Rows >= N lie past the buffer range and arrive as zeros.
-template <int D, int R, bool WITH_Q>
+template <int D, int R, bool WITH_Q, int KT, bool PERM>
 __device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t vbuf, int lane) {
   constexpr int NB = R / 1024;
+  constexpr int LT = (KT - 1) * 16;  // first key of the last 16-key tile
   const int64_t hb = (int64_t)u * p.n * D;
   const uint32_t bytes = (uint32_t)(p.n * D);
   const v4i rk = make_rsrc(p.k + hb, bytes);
   const v4i rv = make_rsrc(p.v + hb, bytes);
   const v4i rq = make_rsrc(p.q + hb, bytes);
+  // K and V rows of the last tile are transposed 4 x 4 (kt_perm): its real
+  // keys fill the accumulator rows r = 0 first, so that every lane's rows
+  // r >= ceil(real keys / 4) hold padding only
+  auto kv_row = [&](int row) { return (PERM && row >= LT && row < LT + 16) ? LT + kt_perm(row - LT) : row; };
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int o = blk * 1024 + 16 * lane;
     const int row = o / D, cp = (o % D) >> 4;
-    const int ko = row * D + 16 * (cp ^ kswz<D>(row));
-    raw_buffer_load_lds(rk, (lds_u32w*)(uintptr_t)(vbuf + R + blk * 1024), 16, ko, 0, 0, 0);
+    const int sw = 16 * (cp ^ kswz<D>(row));
+    raw_buffer_load_lds(rk, (lds_u32w*)(uintptr_t)(vbuf + R + blk * 1024), 16, kv_row(row) * D + sw,
+                        0, 0, 0);
     if (WITH_Q)
-      raw_buffer_load_lds(rq, (lds_u32w*)(uintptr_t)(vbuf + 2 * R + blk * 1024), 16, ko, 0, 0, 0);
+      raw_buffer_load_lds(rq, (lds_u32w*)(uintptr_t)(vbuf + 2 * R + blk * 1024), 16, row * D + sw, 0,
+                          0, 0);
   }
   // V last: the Q.K^T part of a tile may start once the loads above are in
 #pragma unroll
@@ -183,13 +194,21 @@ __device__ __forceinline__ void stage_head(const DevParams& p, int u, uint32_t v
     const int o = blk * 1024 + 16 * lane;
     const int row = o / D, cp = (o % D) >> 4;
     raw_buffer_load_lds(rv, (lds_u32w*)(uintptr_t)(vbuf + blk * 1024), 16,
-                        row * D + 16 * (cp ^ vswz<D>(row)), 0, 0, 0);
+                        kv_row(row) * D + 16 * (cp ^ vswz<D>(row)), 0, 0, 0);
   }
 }
 
 // s_waitcnt immediate for vmcnt(n), other counters untouched (n < 64)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+
+// Output stores of rows of up to 64 keys (many small heads, two workgroups
+// per CU) go through LDS as whole-row chunks with cache policy sc1 (written
+// through while the kernel runs instead of left dirty in L2 for the
+// end-of-kernel write-back); longer rows store each lane's words directly
+// (measured faster there).
+constexpr int kOutStorePolicy = 16;
+constexpr bool fast_staged_out(int kt) { return kt <= 4; }
 
 // Output requantisation and store of a lane's 4 x FT int32 sums (features
 // 16 ft + 4 g + r of one query, at byte offset dst + 16 ft of the head).
@@ -215,6 +234,53 @@ __device__ __forceinline__ void store_out(const DevParams& p, const v4i (&O)[FT]
                          (uint32_t)requant_i8(O[ft][3], p.pv_b, p.pv_c)),
           ores, dst + ft * 16, 0, 0);
   }
+}
+
+
+
+// Output requantisation and store of a tile through LDS: each lane's four
+// words (features 16 ft + 4 g .. + 3 of query row li) go to the wave's own
+// 16 Q rows in LDS (dead once its Q operand is loaded), and the tile leaves as
+// 16-byte chunks of whole rows (one store instruction covers 16 rows).  Rows
+// past N lie outside the output range and are dropped by the buffer store.
+template <int D, int FT>
+__device__ __forceinline__ void store_out_staged(const DevParams& p, const v4i (&O)[FT],
+                                                 __amdgpu_buffer_rsrc_t ores, int8_t* stage,
+                                                 int li, int g, int lane, int row0, int ostride) {
+  uint32_t wd[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    if (p.pv_fast)
+      wd[ft] = pack4_lowbytes((uint32_t)clamp127(mulhi_i32(O[ft][0], p.pv_bm)),
+                              (uint32_t)clamp127(mulhi_i32(O[ft][1], p.pv_bm)),
+                              (uint32_t)clamp127(mulhi_i32(O[ft][2], p.pv_bm)),
+                              (uint32_t)clamp127(mulhi_i32(O[ft][3], p.pv_bm)));
+    else
+      wd[ft] = pack4_lowbytes((uint32_t)requant_i8(O[ft][0], p.pv_b, p.pv_c),
+                              (uint32_t)requant_i8(O[ft][1], p.pv_b, p.pv_c),
+                              (uint32_t)requant_i8(O[ft][2], p.pv_b, p.pv_c),
+                              (uint32_t)requant_i8(O[ft][3], p.pv_b, p.pv_c));
+  }
+  volatile uint32_t* sw = (volatile uint32_t*)(stage + li * D + 4 * g);
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) sw[4 * ft] = wd[ft];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int r = lane >> 2, c = lane & 3;
+  if (D == 64) {
+    const v4i val = *(volatile v4i*)(stage + r * 64 + 16 * c);
+    __builtin_amdgcn_raw_buffer_store_b128(val, ores, (row0 + r) * ostride + 16 * c, 0,
+                                           kOutStorePolicy);
+  } else {
+    const v2i val = *(volatile v2i*)(stage + r * 32 + 8 * c);
+    __builtin_amdgcn_raw_buffer_store_b64(val, ores, (row0 + r) * ostride + 8 * c, 0,
+                                          kOutStorePolicy);
+  }
+  // (the next tile's writes to these rows come after these reads)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int D, int KT, bool BIAS, int VAR>
@@ -243,12 +309,41 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
   // work-queue words: next tile of the workgroup's sequence, then per buffer
   // the item it holds and the number of that item's tiles finished
   int* ctl = (int*)(smem + NBUF * BS + kFastTableBytes + (VAR == kFastLisValu ? CW * 1024 : 0));
+  // windowed bias of 64-key rows staged in LDS (p.bias_lds): [heads][64][64] int32,
+  // the 16-byte chunk c of row r at slot c ^ (r & 15), so that the b128 reads of
+  // sixteen query rows (one chunk each) fall on distinct banks
+  const int32_t* sBias = (const int32_t*)(smem + NBUF * BS + kFastTableBytes +
+                                          (VAR == kFastLisValu ? CW * 1024 : 0) + 64);
+  constexpr bool BIAS64 = BIAS && KT == 4;
+  // last key tile transposed (no bias: the expanded bias keeps the natural
+  // key order of its rows)
+  constexpr bool PERM = !BIAS;
   int* const ctl_next = ctl;
   int* const ctl_ready = ctl + 1;
   int* const ctl_done = ctl + 1 + NBUF;
   int* const ctl_vready = ctl + 1 + 2 * NBUF;  // item whose V is in the buffer
 
-  if (decode_item<KT>(p, blockIdx.x).u < 0) return;  // uniform, before the barrier
+  const Item item0 = decode_item<KT>(p, blockIdx.x);
+  if (item0.u < 0) return;  // uniform, before the barrier
+  if (wave == CW) {
+    // the loader issues its first loads before the barrier (they go to the
+    // table, bias and buffer-0 regions, not to the work-queue words that
+    // thread 0 initialises): the exponential table (entries e << e_shift,
+    // 1 KB), every head's windowed bias for rows of 64 keys (read from L2: it is
+    // the same for every workgroup), then item 0's K, Q and V
+    raw_buffer_load_lds(make_rsrc(p.exp_tab, kFastTableBytes), (lds_u32w*)(uintptr_t)lds_addr(sE),
+                        16, 16 * lane, 0, 0, 0);
+    if (BIAS64 && p.bias_lds) {
+      const v4i rb = make_rsrc(p.bias, (uint32_t)(p.heads * 64 * 64 * 4));
+      const uint32_t b0 = lds_addr(sBias);
+      for (int blk = 0; blk < p.heads * 16; ++blk) {
+        const int row = 4 * blk + (lane >> 4), slot = lane & 15;
+        raw_buffer_load_lds(rb, (lds_u32w*)(uintptr_t)(b0 + blk * 1024), 16,
+                            row * 256 + 16 * (slot ^ (row & 15)), 0, 0, 0);
+      }
+    }
+    stage_head<D, R, QLDS, KT, PERM>(p, item0.u, smem0, lane);
+  }
   if (tid == 0) {
     ctl_next[0] = 0;
 #pragma unroll
@@ -258,15 +353,18 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       ctl_vready[b] = -1;
     }
   }
-  __syncthreads();  // the only workgroup barrier
+  // the only workgroup barrier; it orders the work-queue words that thread 0
+  // wrote (a fence in the loader wave would make it wait for its loads into
+  // LDS first)
+  if (wave != CW) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   if (wave == CW) {
-    // ---- loader wave: the exponential table (entries e << e_shift, 1 KB),
-    //      then item j of the workgroup's sequence into buffer j % NBUF once
-    //      every tile of item j - NBUF is finished; the table is in LDS
-    //      together with item 0
-    raw_buffer_load_lds(make_rsrc(p.exp_tab, kFastTableBytes), (lds_u32w*)(uintptr_t)lds_addr(sE),
-                        16, 16 * lane, 0, 0, 0);
+    // ---- loader wave: item j of the workgroup's sequence into buffer
+    //      j % NBUF once every tile of item j - NBUF is finished (item 0 and
+    //      the table were issued before the barrier; the flags of item 0 cover
+    //      them)
     for (int j = 0;; ++j) {
       const Item it = decode_item<KT>(p, (int)blockIdx.x + j * G);
       if (it.u < 0) break;
@@ -285,8 +383,12 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      if (lane == 0) __hip_atomic_store(&ctl_done[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      stage_head<D, R, QLDS>(p, it.u, smem0 + b * BS, lane);
+      // (the counters start at 0; resetting only reused buffers keeps the
+      // first items' loads from waiting behind a vmcnt(0) the compiler puts
+      // before any LDS access that follows a direct load)
+      if (j >= NBUF && lane == 0)
+        __hip_atomic_store(&ctl_done[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (j > 0) stage_head<D, R, QLDS, KT, PERM>(p, it.u, smem0 + b * BS, lane);
       // (in effect both flags below are set once K, Q and V are all in: the
       // compiler puts a vmcnt(0) before every LDS access that follows a direct
       // load into LDS, the release stores included.  Loaders that set the K/Q
@@ -302,13 +404,17 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
 
   // ---- compute waves
   // padded keys of the last tile held by this lane: accumulator init and count
+  // (with the transposed last tile, row 4 g + r holds key 4 r + g of it, and
+  // rows r >= rl of every lane hold padding only: pass 2 skips them)
+  const int nl = N - (KT - 1) * 16;       // real keys of the last tile, 1..16
+  const int rl = PERM ? (nl + 3) >> 2 : 4;
   v4i cmask;
   int npad = 0;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const bool pad = (KT - 1) * 16 + 4 * g + r >= N;
+    const bool pad = PERM ? 4 * r + g >= nl : (KT - 1) * 16 + 4 * g + r >= N;
     cmask[r] = pad ? p.mask_s : 0;
-    npad += pad ? 1 : 0;
+    npad += (pad && r < rl) ? 1 : 0;
   }
   const int32_t tab0 = (int32_t)lds_addr(sE);  // absolute LDS address of entry 0
   // per-lane operand offsets inside a K region (the swizzle depends on li only)
@@ -366,6 +472,8 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
     // Query rows past N are clamped to N - 1 for every load, bias read and
     // store: such a lane computes query N - 1 exactly and stores the same bytes.
     const __amdgpu_buffer_rsrc_t qres = buf_rsrc(p.q + hbase, (uint32_t)(N * D));
+    const __amdgpu_buffer_rsrc_t bres =
+        buf_rsrc(p.bias, BIAS ? (uint32_t)((int64_t)p.heads * (KT * 16) * (KT * 16) * 4) : 0u);
     // output rows of this head: `ostride` bytes apart (head-major or token-major)
     const int ostride = out_row_stride(p, D);
     const __amdgpu_buffer_rsrc_t ores =
@@ -395,7 +503,14 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
         if (kt + KPF < KT) kb[kt % KPF] = *(const Op*)(sK + (kt + KPF) * 16 * D + koff);
         v4i c0 = {0, 0, 0, 0};
         if (BIAS) {
-          c0 = *(const v4i*)(p.bias + ((int64_t)h * (KT * 16) + qrow) * (KT * 16) + kt * 16 + 4 * g);
+          // (an LDS-typed read and a buffer load: a generic pointer chosen at run
+          // time would become a flat load, which waits for the stores too)
+          if (BIAS64 && p.bias_lds)
+            c0 = *(lds_v4i*)(uintptr_t)(lds_addr(sBias) +
+                                        4u * ((h * 64 + qrow) * 64 + 4 * ((kt * 4 + g) ^ (qrow & 15))));
+          else
+            c0 = __builtin_amdgcn_raw_buffer_load_b128(
+                bres, (int)(((h * (KT * 16) + qrow) * (KT * 16) + kt * 16 + 4 * g) * 4), 0, 0);
         } else if (kt == KT - 1) {
           c0 = cmask;
         }
@@ -438,6 +553,10 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
       for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          if (PERM && kt == KT - 1 && r > 0 && r >= rl) {
+            S[kt][r] = 0;  // padding only: e = 0
+            continue;
+          }
           const int32_t a = exp_offset(S[kt][r], qk_bm, -4, rb, lo, hi);
           const uint32_t e = lds_read_u32((uint32_t)a);
           S[kt][r] = (int32_t)e;
@@ -509,7 +628,11 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           for (int ft = 0; ft < FT; ++ft) vcur[ft] = vnxt[ft];
         }
         // lane holds features 16 ft + 4 g + r of query qrow
-        store_out<FT>(p, O, ores, qrow * ostride + 4 * g);
+        if (QLDS && fast_staged_out(KT))
+          store_out_staged<D, FT>(p, O, ores, const_cast<int8_t*>(sQ) + qt * 16 * D, li, g, lane,
+                                  qt * 16, ostride);
+        else
+          store_out<FT>(p, O, ores, qrow * ostride + 4 * g);
       } else {
         // ---- LIS: Ph = (f e) >> (M - F) as one mulhi, shift w = F - code as
         //      w + 128 (VALU engine: the amount of a 32-bit shift, formed one
@@ -563,7 +686,11 @@ __global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT,
           for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
             for (int r = 0; r < 4; ++r) O0[ft][r] = -(O0[ft][r] + (O1[ft][r] << 8));
-          store_out<FT>(p, O0, ores, qrow * ostride + 4 * g);
+          if (QLDS && fast_staged_out(KT))
+            store_out_staged<D, FT>(p, O0, ores, const_cast<int8_t*>(sQ) + qt * 16 * D, li, g,
+                                    lane, qt * 16, ostride);
+          else
+            store_out<FT>(p, O0, ores, qrow * ostride + 4 * g);
         } else {
           // ---- VALU P.V: lane owns 4 queries x NF = D / 16 features (lanes
           //      16 qg + fg: queries 4 qg.., features NF fg..); the wave's shifts

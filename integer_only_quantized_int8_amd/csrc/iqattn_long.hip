@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void iqattn_long(DevParams p) {
     const Op qop = buf_load<Op>(qres, qrow * D + KPL * g);
     const int32_t* brow = BIAS ? p.bias + ((int64_t)h * Np + qrow) * Np + 4 * g : nullptr;
 
-    // the Q.K^T accumulators of key block kb (tiles kb .. kb + 7 that exist)
+    // the Q.K^T accumulators of key block kb (tiles kb .. kb + 3 that exist)
     auto qk_block = [&](int kb, v4i (&S)[kLongBlk]) {
 #pragma unroll
       for (int t = 0; t < kLongBlk; ++t) {
