@@ -60,6 +60,8 @@ extern "C" {
 #define IQATTN_E_DEVICE      -7  /* no usable gfx950 device is current             */
 #define IQATTN_E_INCOMPLETE  -8  /* a kernel's bounded wait gave up: some output
                                     rows of a launch were not written          */
+#define IQATTN_E_TOOBIG      -9  /* iqattn_forward_noalloc: the windowed bias does
+                                    not fit its static device memory            */
 
 #define IQATTN_SHIFTMAX 0
 #define IQATTN_LIS      1
@@ -159,6 +161,26 @@ int iqattn_set_spin_limit(iqattn_ctx* ctx, int32_t polls);
 /* Free the context's device memory.  NULL is accepted (returns 0).  The
  * caller must make sure no forward using ctx is still running.              */
 int iqattn_destroy(iqattn_ctx* ctx);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * attention of *p in one call that allocates nothing -- no context, no
+ * hipMalloc / hipFree, no allocating library routine.  It enqueues on
+ * `hip_stream` a set-up kernel (exponential table, cleared status word), the
+ * bias expansion when p->rel_bias is set, and the fused kernel of
+ * iqattn_forward; the results are byte-identical to iqattn_create +
+ * iqattn_forward with the same parameters.  q, k, v, out as for
+ * iqattn_forward; p->rel_bias (host memory) is read during the call only.
+ * The device memory it uses is a static array of the library (about 260 KB
+ * per GPU, kept until the process ends) that every call on that GPU shares:
+ * calls that overlap in time on one GPU race (serialise them on one stream).
+ * Limit: p->heads * (2 window - 1)^2 <= 960 and p->heads * 16 ceil(N/16) *
+ * 16 ceil(N/16) * 4 <= 262144 bytes when rel_bias is set (IQATTN_E_TOOBIG
+ * otherwise, checked before any HIP call, like the ranges of iqattn_create).
+ * There is no completion check for these calls (the status word is cleared by
+ * each call).  Returns as iqattn_create and iqattn_forward.                 */
+int iqattn_forward_noalloc(const iqattn_params* p, const int8_t* q, const int8_t* k,
+                           const int8_t* v, int8_t* out, void* hip_stream);
 
 /* Static text for an error code (for IQATTN_E_LAUNCH: the last HIP error
  * seen by this thread).                                                      */

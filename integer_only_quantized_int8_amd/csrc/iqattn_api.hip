@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "iqattn.h"
 #include "iqattn_dev.h"
 
@@ -24,8 +26,10 @@ namespace {
 // e(-idx) << shift for idx = 0..255: the Shiftmax exponential of
 // delta = -idx (I-ViT sec. 3.3) with exp_frac_bits extra fraction bits:
 //   I_p = d + (d >> 1) - (d >> 4);  -I_p = q i0 + r;  e = ((i0 + ((-r) >> 1)) << n) >> q
-__global__ void iqattn_build_exp(uint32_t* tab, int32_t i0, int32_t nfrac, int32_t shift) {
+__global__ void iqattn_build_exp(uint32_t* tab, int32_t i0, int32_t nfrac, int32_t shift,
+                                 uint32_t* status_clear) {
   const int idx = threadIdx.x;
+  if (idx == 0 && status_clear) *status_clear = 0u;
   if (idx > 255) return;
   const int32_t d = -idx;
   const int32_t ip = d + (d >> 1) - (d >> 4);
@@ -48,6 +52,43 @@ __global__ void iqattn_expand_bias(int32_t* out, const int32_t* table, int32_t h
     if (i < n && j < n) {
       const int dr = i / w - j / w, dc = i % w - j % w;
       val = table[(int64_t)h * (2 * w - 1) * (2 * w - 1) + (dr + w - 1) * (2 * w - 1) + dc + w - 1];
+    }
+    out[x] = val;
+  }
+}
+
+// Index of the first zero entry of the table iqattn_build_exp writes (255 if
+// none): the same integer steps on the host, so that no read-back is needed.
+int host_exp_last(int32_t i0, int32_t nfrac, int32_t shift) {
+  for (int idx = 0; idx < 256; ++idx) {
+    const int32_t d = -idx;
+    const int32_t ip = d + (d >> 1) - (d >> 4);
+    const int32_t np = -ip;
+    const int32_t q = np / i0, r = np - q * i0;
+    const int64_t mant = (int64_t)i0 + ((-r) >> 1);
+    const uint64_t e = (q >= 62) ? 0u : (uint64_t)((mant << nfrac) >> q);
+    if ((uint32_t)(e << shift) == 0) return idx;
+  }
+  return 255;
+}
+
+// The relative-position table passed by value (the no-allocation entry point
+// has no device buffer to copy it into).
+constexpr int kArgBiasMax = 960;  // int32 entries: heads * (2w - 1)^2
+struct BiasArg {
+  int32_t v[kArgBiasMax];
+};
+
+__global__ void iqattn_expand_bias_arg(int32_t* out, BiasArg table, int32_t heads, int32_t n,
+                                       int32_t np, int32_t w, int32_t pad) {
+  const int64_t total = (int64_t)heads * np * np;
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(x % np), i = (int)((x / np) % np), h = (int)(x / ((int64_t)np * np));
+    int32_t val = pad;
+    if (i < n && j < n) {
+      const int dr = i / w - j / w, dc = i % w - j % w;
+      val = table.v[h * (2 * w - 1) * (2 * w - 1) + (dr + w - 1) * (2 * w - 1) + dc + w - 1];
     }
     out[x] = val;
   }
@@ -157,11 +198,131 @@ bool fast_constants(const iqattn_params* p, int kt, int64_t bias_max, DevParams*
   return true;
 }
 
-}  // namespace
-
 // Polls of a bounded work-queue wait (each followed by s_sleep 1, about 64
 // clocks) before a wave gives up; only a broken invariant could reach it.
 constexpr int32_t kDefaultSpinLimit = 1 << 22;
+
+// Everything a launch needs except the device pointers: kernel, launch shape,
+// constants.  No device memory is touched.
+struct Plan {
+  DevParams dp;
+  KernelFn fn;
+  size_t lds_bytes;
+  int fast;
+  int grid;
+  int block;  // threads per workgroup
+  int np;     // 16 * number of key tiles (rows of the expanded bias)
+};
+
+int make_plan(const iqattn_params* p, int dev, const hipDeviceProp_t& prop, Plan* pl) {
+  memset(pl, 0, sizeof(*pl));
+  const int N = p->seq_len, D = p->head_dim;
+  const int KT = (N + 15) / 16, KS = (KT + 3) / 4, Np = KT * 16;
+  pl->np = Np;
+  int64_t bias_max = 0;
+  if (p->rel_bias) {
+    const int64_t span = (int64_t)(2 * p->window - 1) * (2 * p->window - 1) * p->heads;
+    for (int64_t i = 0; i < span; ++i) {
+      const int64_t a = p->rel_bias[i] < 0 ? -(int64_t)p->rel_bias[i] : p->rel_bias[i];
+      if (a > bias_max) bias_max = a;
+    }
+  }
+  DevParams& dp = pl->dp;
+  pl->fast = fast_constants(p, KT, bias_max, &dp) ? 1 : 0;
+  dp.exp_last = host_exp_last(p->i0, p->exp_frac_bits, pl->fast ? dp.e_shift : 0);
+  const size_t kbytes = (size_t)Np * (D + 16);
+  if (pl->fast) {
+    // buffers (V, K regions of R bytes each), table, LIS shift scratch; the
+    // last V region's operand reads reach KS * 64 rows past its start
+    const int var = fast_variant(p);
+    const bool bias = p->rel_bias != NULL;
+    const size_t R = (size_t)fast_region_bytes(D, KT);
+    const size_t nbuf = (size_t)fast_nbuf(KT, bias, var);
+    const size_t cw = (size_t)fast_cw(KT, bias);
+    const size_t bs = (size_t)fast_nreg(KT, bias) * R;  // bytes per buffer
+    const size_t used = nbuf * bs + kFastTableBytes + (var == kFastLisValu ? cw * 1024 : 0) + 64;
+    const size_t reach = (nbuf - 1) * bs + (size_t)KS * 64 * D;
+    pl->fn = fast_kernel(D, KT, bias, var);
+    pl->lds_bytes = used > reach ? used : reach;
+    pl->block = (int)(64 * (cw + 1));
+    // rows of 64 keys: the expanded bias of every head in LDS after the
+    // work-queue words, when it fits (the per-tile reads then leave global
+    // memory, where they also waited for the previous tile's stores)
+    const size_t bias_bytes = (size_t)p->heads * 64 * 64 * 4;
+    if (bias && KT == 4 && used + bias_bytes <= 160 * 1024) {
+      dp.bias_lds = 1;
+      pl->lds_bytes = used + bias_bytes;
+    }
+  } else if (KT > 40) {
+    // rows of 641..1024 keys: three passes over LDS-resident K, every back end
+    const int var = fast_variant(p);
+    pl->fn = long_kernel(D, var, p->rel_bias != NULL);
+    pl->block = long_threads();
+    pl->lds_bytes = long_lds_bytes(D, N, var);
+  } else {
+    const size_t vbytes =
+        (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
+    pl->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);
+    pl->block = kThreads;
+    pl->lds_bytes = kbytes + ((vbytes + 15) & ~(size_t)15) + (size_t)(dp.exp_last + 1) * kExpRep * 4 +
+                    (p->variant == IQATTN_LIS ? (size_t)kWaves * 256 * 4 : 0);
+  }
+  int maxlds = 0, optin = 0;
+  (void)hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  (void)hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
+  if (optin > maxlds) maxlds = optin;
+  if ((int64_t)pl->lds_bytes > maxlds) return IQATTN_E_SHAPE;
+  dp.spin_limit = kDefaultSpinLimit;
+  dp.heads = p->heads;
+  dp.n = N;
+  dp.out_tok = p->out_layout == IQATTN_OUT_TOKENS;
+  dp.units = p->batch * p->heads;
+  dp.n_full = dp.units;
+  dp.n_items = dp.units;
+  pl->grid = dp.units;
+  if (pl->fast && dp.units > 0) {
+    // persistent grid: one workgroup per slot the chip holds at once, walking
+    // the work items; the heads of a last, partial round are split into
+    // quarter heads (groups of 8 heads x 4 quarters)
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pl->fn, pl->block,
+                                                     pl->lds_bytes) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    const int64_t slots = (int64_t)per_cu * prop.multiProcessorCount;
+    const int64_t rem = dp.units % slots;
+    if (rem > 0 && rem * 2 <= slots) {
+      dp.n_full = (int32_t)(dp.units - rem);
+      dp.n_items = (int32_t)(dp.n_full + ((rem + 7) / 8) * 32);
+    }
+    pl->grid = (int)(dp.n_items < slots ? dp.n_items : slots);
+  }
+  dp.qk_b = p->qk_b;
+  dp.qk_c = p->qk_c;
+  dp.pv_b = p->pv_b;
+  dp.pv_c = p->pv_c;
+  dp.intdiv_m = p->intdiv_m;
+  dp.p_shift = p->intdiv_m - (p->k_out - 1);
+  dp.p_max = (1 << (p->k_out - 1)) - 1;
+  dp.lis_f = (1 << p->lis_bits) - 1;
+  return IQATTN_OK;
+}
+
+int set_lds_attribute(const Plan& pl) {
+  const hipError_t e = hipFuncSetAttribute((const void*)pl.fn,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)pl.lds_bytes);
+  return e == hipSuccess ? IQATTN_OK : set_hip_error(e, "lds attribute");
+}
+
+int check_device(int* dev, hipDeviceProp_t* prop) {
+  if (hipGetDevice(dev) != hipSuccess) return IQATTN_E_DEVICE;
+  if (hipGetDeviceProperties(prop, *dev) != hipSuccess) return IQATTN_E_DEVICE;
+  if (strncmp(prop->gcnArchName, "gfx950", 6) != 0) return IQATTN_E_DEVICE;
+  return IQATTN_OK;
+}
+
+}  // namespace
 
 struct iqattn_ctx {
   iqattn_params p;
@@ -169,12 +330,7 @@ struct iqattn_ctx {
   uint32_t* exp_tab;
   int32_t* bias;
   uint32_t* status;  // bits of bounded waits that gave up (iqattn_check)
-  KernelFn fn;
-  size_t lds_bytes;
-  DevParams dp;
-  int fast;
-  int grid;
-  int block;  // threads per workgroup
+  Plan pl;
 };
 
 extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
@@ -184,33 +340,21 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
   if (rc) return rc;
 
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return IQATTN_E_DEVICE;
   hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return IQATTN_E_DEVICE;
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return IQATTN_E_DEVICE;
+  if ((rc = check_device(&dev, &prop))) return rc;
 
   iqattn_ctx* c = (iqattn_ctx*)calloc(1, sizeof(iqattn_ctx));
   if (!c) return IQATTN_E_ALLOC;
   c->p = *p;
   c->p.rel_bias = NULL;
   c->device = dev;
-
-  const int N = p->seq_len, D = p->head_dim;
-  const int KT = (N + 15) / 16, KS = (KT + 3) / 4, Np = KT * 16;
-  int64_t bias_max = 0;
-  if (p->rel_bias) {
-    const int64_t span = (int64_t)(2 * p->window - 1) * (2 * p->window - 1) * p->heads;
-    for (int64_t i = 0; i < span; ++i) {
-      const int64_t a = p->rel_bias[i] < 0 ? -(int64_t)p->rel_bias[i] : p->rel_bias[i];
-      if (a > bias_max) bias_max = a;
-    }
-  }
-  c->fast = fast_constants(p, KT, bias_max, &c->dp) ? 1 : 0;
-
+  Plan& pl = c->pl;
   hipError_t e;
+  if ((rc = make_plan(p, dev, prop, &pl))) goto fail;
+  if ((rc = set_lds_attribute(pl))) goto fail;
   if (hipMalloc((void**)&c->exp_tab, 256 * sizeof(uint32_t)) != hipSuccess) {
-    free(c);
-    return IQATTN_E_ALLOC;
+    rc = IQATTN_E_ALLOC;
+    goto fail;
   }
   if (hipMalloc((void**)&c->status, sizeof(uint32_t)) != hipSuccess) { rc = IQATTN_E_ALLOC; goto fail; }
   if ((e = hipMemset(c->status, 0, sizeof(uint32_t))) != hipSuccess) {
@@ -218,11 +362,11 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
     goto fail;
   }
   hipLaunchKernelGGL(iqattn_build_exp, dim3(1), dim3(256), 0, 0, c->exp_tab, p->i0,
-                     p->exp_frac_bits, c->fast ? c->dp.e_shift : 0);
+                     p->exp_frac_bits, pl.fast ? pl.dp.e_shift : 0, (uint32_t*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) { rc = set_hip_error(e, "build_exp"); goto fail; }
   if (p->rel_bias) {
     const size_t tbytes = (size_t)p->heads * (2 * p->window - 1) * (2 * p->window - 1) * 4;
-    const size_t ebytes = (size_t)p->heads * Np * Np * 4;
+    const size_t ebytes = (size_t)p->heads * pl.np * pl.np * 4;
     int32_t* tab = NULL;
     if (hipMalloc((void**)&c->bias, ebytes) != hipSuccess) { rc = IQATTN_E_ALLOC; goto fail; }
     if (hipMalloc((void**)&tab, tbytes) != hipSuccess) { rc = IQATTN_E_ALLOC; goto fail; }
@@ -231,13 +375,14 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
       rc = set_hip_error(e, "bias copy");
       goto fail;
     }
-    hipLaunchKernelGGL(iqattn_expand_bias, dim3(256), dim3(256), 0, 0, c->bias, tab, p->heads, N,
-                       Np, p->window, c->fast ? c->dp.mask_s : 0);
+    hipLaunchKernelGGL(iqattn_expand_bias, dim3(256), dim3(256), 0, 0, c->bias, tab, p->heads,
+                       p->seq_len, pl.np, p->window, pl.fast ? pl.dp.mask_s : 0);
     e = hipDeviceSynchronize();
     (void)hipFree(tab);
     if (e != hipSuccess) { rc = set_hip_error(e, "expand_bias"); goto fail; }
   }
   {
+    // the table on the device must end where the host expects it to
     uint32_t host_tab[256];
     if ((e = hipMemcpy(host_tab, c->exp_tab, sizeof(host_tab), hipMemcpyDeviceToHost)) !=
         hipSuccess) {
@@ -247,94 +392,16 @@ extern "C" int iqattn_create(const iqattn_params* p, iqattn_ctx** out) {
     int last = 255;
     for (int i = 0; i < 256; ++i)
       if (host_tab[i] == 0) { last = i; break; }
-    c->dp.exp_last = last;
-  }
-  {
-    const size_t kbytes = (size_t)Np * (D + 16);
-    size_t vbytes;
-    if (c->fast) {
-      // buffers (V, K regions of R bytes each), table, LIS shift scratch; the
-      // last V region's operand reads reach KS * 64 rows past its start
-      const int var = fast_variant(p);
-      const bool bias = p->rel_bias != NULL;
-      const size_t R = (size_t)fast_region_bytes(D, KT);
-      const size_t nbuf = (size_t)fast_nbuf(KT, bias, var);
-      const size_t cw = (size_t)fast_cw(KT, bias);
-      const size_t bs = (size_t)fast_nreg(KT, bias) * R;  // bytes per buffer
-      const size_t used = nbuf * bs + kFastTableBytes + (var == kFastLisValu ? cw * 1024 : 0) + 64;
-      const size_t reach = (nbuf - 1) * bs + (size_t)KS * 64 * D;
-      c->fn = fast_kernel(D, KT, bias, var);
-      c->lds_bytes = used > reach ? used : reach;
-      c->block = (int)(64 * (cw + 1));
-      // rows of 64 keys: the expanded bias of every head in LDS after the
-      // work-queue words, when it fits (the per-tile reads then leave global
-      // memory, where they also waited for the previous tile's stores)
-      const size_t bias_bytes = (size_t)p->heads * 64 * 64 * 4;
-      if (bias && KT == 4 && used + bias_bytes <= 160 * 1024) {
-        c->dp.bias_lds = 1;
-        c->lds_bytes = used + bias_bytes;
-      }
-    } else if (KT > 40) {
-      // rows of 641..1024 keys: three passes over LDS-resident K, every back end
-      const int var = fast_variant(p);
-      c->fn = long_kernel(D, var, p->rel_bias != NULL);
-      c->block = long_threads();
-      c->lds_bytes = long_lds_bytes(D, N, var);
-    } else {
-      vbytes = (p->variant == IQATTN_SHIFTMAX) ? (size_t)D * (KS * 64 + 16) : (size_t)Np * D;
-      c->fn = generic_kernel(D, KT, p->variant, p->rel_bias != NULL);
-      c->block = kThreads;
-      c->lds_bytes = kbytes + ((vbytes + 15) & ~(size_t)15) +
-                     (size_t)(c->dp.exp_last + 1) * kExpRep * 4 +
-                     (p->variant == IQATTN_LIS ? (size_t)kWaves * 256 * 4 : 0);
-    }
-    int maxlds = 0, optin = 0;
-    (void)hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-    (void)hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev);
-    if (optin > maxlds) maxlds = optin;
-    if ((int64_t)c->lds_bytes > maxlds) { rc = IQATTN_E_SHAPE; goto fail; }
-    if ((e = hipFuncSetAttribute((const void*)c->fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)c->lds_bytes)) != hipSuccess) {
-      rc = set_hip_error(e, "lds attribute");
+    if (last != pl.dp.exp_last) {
+      snprintf(g_errbuf, sizeof(g_errbuf), "exponential table ends at %d, host expects %d", last,
+               pl.dp.exp_last);
+      rc = IQATTN_E_LAUNCH;
       goto fail;
     }
   }
-  c->dp.exp_tab = c->exp_tab;
-  c->dp.bias = c->bias;
-  c->dp.status = c->status;
-  c->dp.spin_limit = kDefaultSpinLimit;
-  c->dp.heads = p->heads;
-  c->dp.n = N;
-  c->dp.out_tok = p->out_layout == IQATTN_OUT_TOKENS;
-  c->dp.units = p->batch * p->heads;
-  c->dp.n_full = c->dp.units;
-  c->dp.n_items = c->dp.units;
-  c->grid = c->dp.units;
-  if (c->fast && c->dp.units > 0) {
-    // persistent grid: one workgroup per slot the chip holds at once, walking
-    // the work items; the heads of a last, partial round are split into
-    // quarter heads (groups of 8 heads x 4 quarters)
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)c->fn, c->block,
-                                                     c->lds_bytes) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
-    const int64_t slots = (int64_t)per_cu * prop.multiProcessorCount;
-    const int64_t rem = c->dp.units % slots;
-    if (rem > 0 && rem * 2 <= slots) {
-      c->dp.n_full = (int32_t)(c->dp.units - rem);
-      c->dp.n_items = (int32_t)(c->dp.n_full + ((rem + 7) / 8) * 32);
-    }
-    c->grid = (int)(c->dp.n_items < slots ? c->dp.n_items : slots);
-  }
-  c->dp.qk_b = p->qk_b;
-  c->dp.qk_c = p->qk_c;
-  c->dp.pv_b = p->pv_b;
-  c->dp.pv_c = p->pv_c;
-  c->dp.intdiv_m = p->intdiv_m;
-  c->dp.p_shift = p->intdiv_m - (p->k_out - 1);
-  c->dp.p_max = (1 << (p->k_out - 1)) - 1;
-  c->dp.lis_f = (1 << p->lis_bits) - 1;
+  pl.dp.exp_tab = c->exp_tab;
+  pl.dp.bias = c->bias;
+  pl.dp.status = c->status;
   if ((e = hipDeviceSynchronize()) != hipSuccess) { rc = set_hip_error(e, "create"); goto fail; }
   *out = c;
   return IQATTN_OK;
@@ -349,18 +416,118 @@ fail:
 extern "C" int iqattn_forward(iqattn_ctx* c, const int8_t* q, const int8_t* k, const int8_t* v,
                               int8_t* out, void* hip_stream) {
   if (!c) return IQATTN_E_NULL;
-  if (c->dp.units == 0) return IQATTN_OK;
+  if (c->pl.dp.units == 0) return IQATTN_OK;
   if (!q || !k || !v || !out) return IQATTN_E_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return IQATTN_E_ALIGN;
-  DevParams dp = c->dp;
+  DevParams dp = c->pl.dp;
   dp.q = q;
   dp.k = k;
   dp.v = v;
   dp.out = out;
-  hipLaunchKernelGGL(c->fn, dim3(c->grid), dim3(c->block), c->lds_bytes,
+  hipLaunchKernelGGL(c->pl.fn, dim3(c->pl.grid), dim3(c->pl.block), c->pl.lds_bytes,
                      (hipStream_t)hip_stream, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqattn launch");
+  return IQATTN_OK;
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+// Static device memory of iqattn_forward_noalloc (one copy per GPU, held until
+// the process ends): the exponential table, the status word and the expanded
+// windowed bias.  Host code never uses the symbol itself as an address (on the
+// host it is only a stand-in): each device's address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kScratchTab = 0;          // 256 u32
+constexpr size_t kScratchStatus = 1024;    // u32 status word
+constexpr size_t kScratchBias = 4096;      // expanded bias, heads * Np * Np int32
+constexpr size_t kScratchBiasBytes = (size_t)256 << 10;
+static __device__ __align__(256) uint8_t scratch[kScratchBias + kScratchBiasBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct DeviceState {
+  bool ready;
+  int rc;
+  uint8_t* scratch;  // device address of `scratch` on this device
+  hipDeviceProp_t prop;
+};
+DeviceState g_dev[kMaxDevices];
+std::mutex g_dev_mutex;
+
+// Set-up of the current device, once: its properties and the device address of
+// its copy of `scratch`.
+int device_state(DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return IQATTN_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  DeviceState& st = g_dev[dev];
+  if (!st.ready) {
+    int d2 = 0;
+    st.rc = check_device(&d2, &st.prop);
+    if (st.rc == IQATTN_OK) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr)
+        st.rc = set_hip_error(e == hipSuccess ? hipErrorInvalidSymbol : e, "scratch address");
+      st.scratch = (uint8_t*)ptr;
+    }
+    st.ready = true;
+  }
+  *out = &st;
+  return st.rc;
+}
+}  // namespace
+
+extern "C" int iqattn_forward_noalloc(const iqattn_params* p, const int8_t* q, const int8_t* k,
+                                      const int8_t* v, int8_t* out, void* hip_stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (p->batch == 0) return IQATTN_OK;
+  if (!q || !k || !v || !out) return IQATTN_E_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return IQATTN_E_ALIGN;
+  // sizes the static memory holds: the relative table travels as a kernel
+  // argument, its expansion lives in `scratch`
+  if (p->rel_bias) {
+    const int64_t span = (int64_t)(2 * p->window - 1) * (2 * p->window - 1) * p->heads;
+    const int64_t np = ((int64_t)p->seq_len + 15) / 16 * 16;
+    if (span > kArgBiasMax || (int64_t)p->heads * np * np * 4 > (int64_t)kScratchBiasBytes)
+      return IQATTN_E_TOOBIG;
+  }
+  DeviceState* st = nullptr;
+  if ((rc = device_state(&st))) return rc;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  Plan pl;
+  if ((rc = make_plan(p, dev, st->prop, &pl))) return rc;
+  if ((rc = set_lds_attribute(pl))) return rc;
+  uint32_t* tab = (uint32_t*)(st->scratch + kScratchTab);
+  uint32_t* status = (uint32_t*)(st->scratch + kScratchStatus);
+  int32_t* bias = (int32_t*)(st->scratch + kScratchBias);
+  hipStream_t stream = (hipStream_t)hip_stream;
+  // the table and a cleared status word (a kernel, not a memset: callers may
+  // capture this call in a graph), then the expanded bias, then the attention
+  hipLaunchKernelGGL(iqattn_build_exp, dim3(1), dim3(256), 0, stream, tab, p->i0,
+                     p->exp_frac_bits, pl.fast ? pl.dp.e_shift : 0, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_hip_error(e, "build_exp");
+  if (p->rel_bias) {
+    BiasArg ba;
+    const int span = (2 * p->window - 1) * (2 * p->window - 1) * p->heads;
+    memcpy(ba.v, p->rel_bias, (size_t)span * sizeof(int32_t));
+    hipLaunchKernelGGL(iqattn_expand_bias_arg, dim3(64), dim3(256), 0, stream, bias, ba, p->heads,
+                       p->seq_len, pl.np, p->window, pl.fast ? pl.dp.mask_s : 0);
+    if ((e = hipGetLastError()) != hipSuccess) return set_hip_error(e, "expand_bias");
+  }
+  DevParams dp = pl.dp;
+  dp.exp_tab = tab;
+  dp.bias = p->rel_bias ? bias : nullptr;
+  dp.status = status;
+  dp.q = q;
+  dp.k = k;
+  dp.v = v;
+  dp.out = out;
+  hipLaunchKernelGGL(pl.fn, dim3(pl.grid), dim3(pl.block), pl.lds_bytes, stream, dp);
+  if ((e = hipGetLastError()) != hipSuccess) return set_hip_error(e, "iqattn launch");
   return IQATTN_OK;
 }
 
@@ -381,7 +548,7 @@ extern "C" int iqattn_check(iqattn_ctx* c, void* hip_stream) {
 extern "C" int iqattn_set_spin_limit(iqattn_ctx* c, int32_t polls) {
   if (!c) return IQATTN_E_NULL;
   if (polls < 1) return IQATTN_E_INVAL;
-  c->dp.spin_limit = polls;
+  c->pl.dp.spin_limit = polls;
   return IQATTN_OK;
 }
 
@@ -409,6 +576,8 @@ extern "C" const char* iqattn_strerror(int code) {
     case IQATTN_E_ALIGN: return "tensor pointer not 16-byte aligned";
     case IQATTN_E_DEVICE: return "no usable gfx950 device";
     case IQATTN_E_INCOMPLETE: return "a bounded wait in the kernel gave up: output incomplete";
+    case IQATTN_E_TOOBIG:
+      return "the windowed bias exceeds the static memory of iqattn_forward_noalloc";
     default: return "unknown error code";
   }
 }

@@ -26,6 +26,7 @@ IQATTN_E_NULL = -5
 IQATTN_E_ALIGN = -6
 IQATTN_E_DEVICE = -7
 IQATTN_E_INCOMPLETE = -8
+IQATTN_E_TOOBIG = -9
 IQATTN_SHIFTMAX = 0
 IQATTN_LIS = 1
 IQATTN_OUT_HEADS = 0
@@ -37,7 +38,7 @@ IQLINEAR_PLAIN = 0
 IQLINEAR_QKV_HEADS = 1
 
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
-            "iqattn_check", "iqattn_set_spin_limit",
+            "iqattn_check", "iqattn_set_spin_limit", "iqattn_forward_noalloc",
             "iqlinear_create", "iqlinear_forward", "iqlinear_destroy", "iqlinear_check",
             "iqlinear_set_spin_limit",
             "iqgelu_create", "iqgelu_forward", "iqgelu_destroy",
@@ -103,6 +104,8 @@ def load_library():
         lib.iqattn_check.restype = C.c_int
         lib.iqattn_set_spin_limit.argtypes = [C.c_void_p, C.c_int32]
         lib.iqattn_set_spin_limit.restype = C.c_int
+        lib.iqattn_forward_noalloc.argtypes = [C.POINTER(iqattn_params)] + [C.c_void_p] * 5
+        lib.iqattn_forward_noalloc.restype = C.c_int
         lib.iqlinear_create.argtypes = [C.POINTER(iqlinear_params), C.POINTER(C.c_void_p)]
         lib.iqlinear_create.restype = C.c_int
         lib.iqlinear_forward.argtypes = [C.c_void_p] * 7
@@ -195,6 +198,18 @@ def iqattn_check(ctx: int, stream=None) -> int:
     if rc not in (IQATTN_OK, IQATTN_E_INCOMPLETE):
         raise IQAttnError(rc, "iqattn_check")
     return rc
+
+
+def iqattn_forward_noalloc(shape, params: Dict[str, object], q, k, v, out, stream=None) -> None:
+    """The attention of (shape, params) in one call that allocates nothing
+    (static device memory of the library; calls that overlap on one GPU race)."""
+    p, keep = make_params(shape, params)
+    ptr = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+    rc = load_library().iqattn_forward_noalloc(C.byref(p), ptr(q), ptr(k), ptr(v), ptr(out),
+                                               C.c_void_p(_stream_handle(stream)))
+    del keep
+    if rc != IQATTN_OK:
+        raise IQAttnError(rc, "iqattn_forward_noalloc")
 
 
 def iqattn_set_spin_limit(ctx: int, polls: int) -> None:

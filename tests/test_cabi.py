@@ -44,7 +44,7 @@ def test_header_constants_match_binding():
                  "IQATTN_E_LAUNCH", "IQATTN_E_NULL", "IQATTN_E_ALIGN", "IQATTN_E_DEVICE",
                  "IQATTN_SHIFTMAX", "IQATTN_LIS", "IQATTN_LIS_VALU", "IQATTN_LIS_MFMA",
                  "IQATTN_OUT_HEADS", "IQATTN_OUT_TOKENS", "IQATTN_MAX_SEQ",
-                 "IQATTN_E_INCOMPLETE"):
+                 "IQATTN_E_INCOMPLETE", "IQATTN_E_TOOBIG"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(IQ, name), name
     text = open(os.path.join(ROOT, "include", "iqlinear.h")).read()
@@ -105,7 +105,7 @@ def test_null_pointers_and_destroy_null(lib):
 
 
 def test_strerror_texts(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -99):
         s = IQ.iqattn_strerror(code)
         assert isinstance(s, str) and s
 
@@ -266,3 +266,31 @@ def test_struct_layouts_match_headers():
         assert got[(name, "size")] == C.sizeof(cls), name
         for field, _ in cls._fields_:
             assert got[(name, field)] == getattr(cls, field).offset, (name, field)
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    """iqattn_forward_noalloc checks ranges, pointers and its static-memory
+    limits before any HIP call (no device here)."""
+    params = W.default_params(3)
+    fake = C.c_void_p(16 * 1024)
+    def call(shape, **over):
+        p, keep = IQ.make_params(shape, dict(params, **over))
+        rc = lib.iqattn_forward_noalloc(C.byref(p), fake, fake, fake, fake, None)
+        del keep
+        return rc
+    assert call((1, 1, 1025, 64)) == IQ.IQATTN_E_SHAPE
+    assert call((1, 1, 16, 64), qk_b=0) == IQ.IQATTN_E_INVAL
+    assert call((0, 1, 16, 64)) == IQ.IQATTN_OK          # empty batch: nothing to do
+    p, keep = IQ.make_params((1, 1, 16, 64), params)
+    assert lib.iqattn_forward_noalloc(C.byref(p), None, fake, fake, fake, None) == IQ.IQATTN_E_NULL
+    bad = C.c_void_p(16 * 1024 + 3)
+    assert lib.iqattn_forward_noalloc(C.byref(p), bad, fake, fake, fake, None) == IQ.IQATTN_E_ALIGN
+    # the windowed bias: relative tables of more than 960 entries
+    assert call((1, 20, 49, 32), window=7, rel_bias=np.zeros((20, 169), np.int32)) == \
+        IQ.IQATTN_E_TOOBIG
+    assert call((1, 2, 400, 32), window=20, rel_bias=np.zeros((2, 39 * 39), np.int32)) == \
+        IQ.IQATTN_E_TOOBIG
+    # within the limits the call gets as far as the device
+    assert call((1, 3, 49, 32), window=7, rel_bias=np.zeros((3, 169), np.int32)) == \
+        IQ.IQATTN_E_DEVICE
+    assert call((2, 3, 197, 64)) == IQ.IQATTN_E_DEVICE
