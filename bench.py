@@ -51,13 +51,58 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def _load_record(kind: str, workload: str):
+    """A committed counter record of profiles/, or None when it is missing or
+    belongs to other attention sources."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
+    return rec
+
+
+def load_traffic(workload: str):
+    return _load_record("traffic", workload)
+
+
+def load_counters(workload: str):
+    return _load_record("counters", workload)
+
+
+# one rocprofv3 --pmc pass: every counter of it, averaged over the attention
+# kernel's dispatches (GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles)
+UNIT_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4
+
+
+def record_counters(csv_path: str, workload: str) -> dict:
+    """Per-dispatch unit counters of the attention kernel from a rocprofv3 --pmc
+    counter file, with the figures derived from them."""
+    import csv
+    sums, counts = {}, {}
+    kernel = None
+    for r in csv.DictReader(open(csv_path)):
+        if not _is_attention_kernel(r["Kernel_Name"]):
+            continue
+        kernel = r["Kernel_Name"]
+        c = r["Counter_Name"]
+        sums[c] = sums.get(c, 0.0) + float(r["Counter_Value"])
+        counts[c] = counts.get(c, 0) + 1
+    if not sums:
+        raise SystemExit(f"{csv_path}: no attention-kernel dispatches")
+    avg = {c: sums[c] / counts[c] for c in sums}
+    valu = avg["SQ_INSTS_VALU"] - avg.get("SQ_INSTS_MFMA", 0.0)
+    xcd_cycles = avg["GRBM_GUI_ACTIVE"] / 8.0
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_sha256_16": kernel_source_hash(),
+           "dispatches": min(counts.values()), "per_dispatch": {c: round(v) for c, v in avg.items()},
+           "valu_insts_per_launch": round(valu),
+           # wave64 VALU instructions x 4 cycles (16 lanes per cycle) per SIMD over the
+           # dispatch's busy cycles, and the matrix cores' busy share
+           "valu_busy_share": round(4.0 * valu / SIMDS / xcd_cycles, 4),
+           "mfma_busy_share": round(avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / SIMDS / xcd_cycles, 4)}
     return rec
 
 
@@ -312,6 +357,16 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def workload_name(args) -> str:
+    """Name of the benchmarked workload (the LIS shape with the MFMA engine
+    carries an _mfma suffix)."""
+    from integer_only_quantized_int8_amd import workloads as W
+    name = W.CONFIGS[args.config]["name"]
+    if args.lis_engine == 1:
+        name += "_mfma"
+    return name
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,13 +388,23 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter files and exit (no GPU use)")
+    ap.add_argument("--record-counters", metavar="PMC_CSV",
+                    help="write profiles/counters_<workload>.json from a rocprofv3 --pmc file of "
+                         "the unit counters (" + " ".join(UNIT_COUNTERS) + ") and exit")
+    ap.add_argument("--lis-engine", type=int, default=None, choices=(0, 1),
+                    help="P.V engine of the Log-Int-Softmax shape (0 VALU shift-add, 1 MFMA bit planes)")
+    ap.add_argument("--cold-sets", type=int, default=5,
+                    help="input sets rotated through the cold-cache timing (0 = skip)")
     args = ap.parse_args()
 
-    if args.record_traffic:
-        from integer_only_quantized_int8_amd import workloads as W
-        name = W.CONFIGS[args.config]["name"]
-        rec = record_traffic(args.record_traffic[0], args.record_traffic[1], name)
-        out = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if args.record_traffic or args.record_counters:
+        name = workload_name(args)
+        if args.record_traffic:
+            rec = record_traffic(args.record_traffic[0], args.record_traffic[1], name)
+            out = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+        else:
+            rec = record_counters(args.record_counters, name)
+            out = os.path.join(ROOT, "profiles", f"counters_{name}.json")
         os.makedirs(os.path.dirname(out), exist_ok=True)
         with open(out, "w") as f:
             json.dump(rec, f, indent=1)
@@ -369,6 +434,9 @@ def main():
 
     t0 = time.time()
     w = W.config_workload(args.config)
+    if args.lis_engine is not None:
+        w.params["lis_engine"] = args.lis_engine
+    wname = workload_name(args)
     B, H, N, d = w.q.shape
     heads = B * H
     print(f"[bench] generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -417,6 +485,33 @@ def main():
     kern_ms = graph_step_ms
     del graph
 
+    # cold caches: the same launches rotating over `cold_sets` copies of the
+    # inputs and outputs (more bytes than the 256 MB Infinity Cache), so that
+    # each launch reads its operands from HBM; reported beside the headline
+    cold = None
+    if args.cold_sets > 0:
+        sets = [(q.clone(), k.clone(), v.clone(), torch.empty_like(out))
+                for _ in range(args.cold_sets)]
+        torch.cuda.synchronize()
+        gc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gc):
+            for i in range(args.steps):
+                cq, ck, cv, co = sets[i % len(sets)]
+                att.forward(cq, ck, cv, co)
+        gc.replay()
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        gc.replay()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = c0.elapsed_time(c1) / args.steps
+        rot = len(sets) * 4 * q.numel()
+        same_cold = all(torch.equal(s_[3], out) for s_ in sets)
+        del gc, sets
+        cold = {"input_sets": args.cold_sets, "bytes_in_rotation": int(rot),
+                "kernel_us_mean": round(cold_ms * 1e3, 3), "outputs_equal_hot": bool(same_cold)}
+
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -433,9 +528,13 @@ def main():
     achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
 
     traffic = None
-    trec = load_traffic(w.name)
+    trec = load_traffic(wname)
     if trec is not None:
         traffic = trec["hbm_bytes_per_launch"]
+    crec = load_counters(wname)
+    if cold is not None:
+        cold_gbs = alg_bytes / (cold["kernel_us_mean"] * 1e-6) / 1e9
+        cold.update({"achieved_gbs": round(cold_gbs, 1), "frac": round(cold_gbs / HBM_PEAK_GBS, 4)})
 
     result = {
         "metric": METRIC if args.config == 2 else f"integer-only MSA int8 TOPS, {w.name}",
@@ -450,7 +549,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded int8 Q/K/V, ViT-B/DeiT-B-shaped; no dataset or weights)",
-        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
+        "config": {"workload": wname, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
                    "variant": "lis" if w.params["variant"] == 1 else "shiftmax",
                    "seed": 1000 + args.config, "parallelism": "none (1 GPU)"},
         "kernel_us_mean": round(kern_ms * 1e3, 3),
@@ -465,6 +564,28 @@ def main():
                                    "peak_tops": MFMA_I8_PEAK_TOPS,
                                    "frac": round(ops / (kern_ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}},
     }
+    # the third roofline, from the committed unit-counter record of these
+    # sources: executed VALU instructions (MFMA excluded) x 64 lanes over the
+    # live launch time, against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+    hbm_frac = result["roofline"]["frac"]
+    mfma_frac = result["roofline"]["mfma_int8"]["frac"]
+    valu = None
+    if crec is not None:
+        lane_ops = crec["valu_insts_per_launch"] * 64.0
+        valu_tops = lane_ops / (kern_ms * 1e-3) / 1e12
+        valu = {"achieved_tops": round(valu_tops, 2), "peak_tops": round(VALU_LANE_PEAK_TOPS, 2),
+                "frac": round(valu_tops / VALU_LANE_PEAK_TOPS, 4),
+                "valu_insts_per_launch": crec["valu_insts_per_launch"],
+                "counter_busy_share": crec["valu_busy_share"],
+                "mfma_busy_share": crec["mfma_busy_share"],
+                "source": f"profiles/counters_{wname}.json"}
+        result["roofline"]["valu"] = valu
+    fracs = {"hbm": hbm_frac, "mfma": mfma_frac}
+    if valu is not None:
+        fracs["valu"] = valu["frac"]
+    result["roofline"]["busiest_unit"] = max(fracs, key=fracs.get)
+    if cold is not None:
+        result["cold_hbm"] = cold
     if w.params["variant"] == 1 and int(w.params.get("lis_engine", 0)) == 0:
         # the LIS BitShift P.V on the VALU: one shift-add per (query, key,
         # feature), N^2 d per head, bounds this launch (HBM and MFMA stay listed)
@@ -477,7 +598,9 @@ def main():
             "algorithmic_shift_adds_per_launch": int(shifts),
             "hbm": {"achieved_gbs": hbm["achieved"], "peak_gbs": HBM_PEAK_GBS, "frac": hbm["frac"],
                     "algorithmic_bytes_per_launch": hbm["algorithmic_bytes_per_launch"]},
-            "mfma_int8": hbm["mfma_int8"]}
+            "mfma_int8": hbm["mfma_int8"], "busiest_unit": "alu"}
+        if valu is not None:
+            result["roofline"]["valu"] = valu
 
     if not args.no_cpu:
         import oracle
