@@ -85,7 +85,7 @@ def draw_attention(i):
             window = int(rng.integers(1, 26))
             N = window * window
         else:
-            N = int(rng.integers(1, 641))
+            N = int(rng.integers(1, 1025))
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
     # inputs: spread 1 to 128 (specialised shapes 8 to 128: below that the
     # logit pair b / 2^c passes 1/2 and the generic kernel takes the call)
