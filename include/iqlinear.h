@@ -59,8 +59,8 @@ typedef struct iqlinear_params {
 typedef struct iqlinear_ctx iqlinear_ctx;
 
 /* Validate *p and pick the kernel for the current HIP device.  Synchronous;
- * allocates the context and its 4-byte device status word (see
- * iqlinear_check).  *out is NULL on error.                                   */
+ * allocates the context and its device tile table (8 bytes per output tile of
+ * 256 x 128 or 128 x 128).  *out is NULL on error.                           */
 int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out);
 
 /* Enqueue Y = requant(X W^T) on `hip_stream` (a hipStream_t; NULL = null
@@ -68,22 +68,11 @@ int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out);
  * tensors; out0 (and out1, out2 for QKV_HEADS) are caller-owned int8 device
  * outputs that do not overlap the inputs.  All pointers 16-byte aligned.
  * Asynchronous, allocates nothing.  IQATTN_E_NULL / IQATTN_E_ALIGN for bad
- * pointers, IQATTN_E_LAUNCH when the launch fails.                          */
+ * pointers, IQATTN_E_LAUNCH when the launch fails.  The kernel's waves wait
+ * for each other only at workgroup barriers (no polled waits), so a launch
+ * that starts runs to completion.  Launches of one context may overlap.     */
 int iqlinear_forward(iqlinear_ctx* ctx, const int8_t* x, const int8_t* w, int8_t* out0,
                      int8_t* out1, int8_t* out2, void* hip_stream);
-
-/* Completion check of the launches enqueued so far: the pipelined kernel's
- * waves wait for their operand stages with bounded polls, and a wave whose
- * poll gives up leaves its output tiles unwritten and sets a bit in the
- * context's status word (a device atomic).  Synchronises `hip_stream`, reads
- * and clears the word; returns IQATTN_OK, IQATTN_E_INCOMPLETE or
- * IQATTN_E_LAUNCH.                                                           */
-int iqlinear_check(iqlinear_ctx* ctx, void* hip_stream);
-
-/* Diagnostic hook for tests of the failure path: every bounded poll of later
- * launches gives up after `polls` polls (>= 1; default 4194304).  Returns
- * IQATTN_E_INVAL for polls < 1.                                              */
-int iqlinear_set_spin_limit(iqlinear_ctx* ctx, int32_t polls);
 
 /* Free the context (NULL accepted).                                          */
 int iqlinear_destroy(iqlinear_ctx* ctx);

@@ -5,17 +5,10 @@
 // Linear Operations" (integer product, then (b * acc) >> c to int8); sec. 3.1
 // (the MSA projections).
 //
-// Kernel (iqlinear_pipe below): persistent workgroups, one per CU, of 4 MFMA
-// waves and 4 loader waves.  Each workgroup computes 128 x 128 output tiles as
-// Y^T = W . X^T with v_mfma_i32_16x16x64_i8, so a lane ends
-// with 4 adjacent output columns of one row (one 4-byte store after the fused
-// requantisation, straight into the head-split layout when asked).  Each
-// compute wave owns a quarter of the tile (64 x 64: 16 MFMA tiles, 64
-// accumulators).  The k loop runs through a ring of LDS stages of 128 k-bytes a
-// row (whole cache lines per load request), filled by the loader waves with
-// direct global->LDS loads; the 16-byte chunks of a 128-byte LDS row are
-// XOR-swizzled by (row >> 1) & 7, which makes the b128 operand reads of 16
-// rows bank-conflict free.
+// Kernel (iqlinear_tile below): Y^T = W . X^T with v_mfma_i32_16x16x64_i8,
+// so a lane ends with 4 adjacent output columns of one row; the requantised
+// bytes of 16-row blocks go through LDS and leave as 16-byte row chunks,
+// straight into the head-split layout when asked.
 #include "iqattn_dev.h"
 #include "iqattn.h"
 #include "iqlinear.h"
@@ -24,6 +17,7 @@
 #include <string.h>
 
 #include <type_traits>
+#include <vector>
 
 namespace iqattn {
 namespace {
@@ -50,14 +44,9 @@ struct LinParams {
   // (Granlund and Montgomery's division by an invariant integer)
   uint32_t seq_magic;
   int32_t seq_shift;
-  uint32_t* status;    // context status word: bit 0 loader, bit 1 compute wave gave up
-  int32_t spin_limit;  // polls of a bounded wait before it gives up
+  const int2* order;   // tile table: (row tile, column tile) of tile index t
+  int32_t ntiles;
 };
-
-__device__ __forceinline__ void lin_giveup(const LinParams& p, uint32_t bit) {
-  if ((threadIdx.x & 63) == 0)
-    __hip_atomic_fetch_or(p.status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <typename T>
 __device__ __forceinline__ T pick3(int which, T a0, T a1, T a2) {
@@ -143,313 +132,247 @@ __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[
   }
 }
 
-// The same epilogue through a wave-private LDS block: the requantised bytes of
-// the wave's (16 TM) x (16 TN) block go to LDS rows of kEpPitch bytes (the
-// pitch keeps the 4-byte writes of 16 rows bank-conflict free), then each lane
-// stores whole 16-byte row chunks (4 x fewer store instructions, contiguous
-// 16-byte writes).  Needs 16-column groups that stay inside one output row
-// segment: always for the plain layout, head_dim % 16 == 0 for the head split.
-// The pair of a 16-column group is wave-uniform (n_w is), so it is picked from
-// scalar registers; the output tensor of a lane's chunk is picked by selects.
-constexpr int kEpPitch = 16 * 4 + 16;  // (16 TN = 64) bytes + 16 of padding
+// Row pitch of a wave's LDS output block: 64 bytes of a 16 x 64 block plus
+// 16 of padding, which keeps the 4-byte writes of 16 rows bank-conflict free.
+constexpr int kEpPitch = 16 * 4 + 16;
 
-// Window path, four 4-column blocks at once: byte r of word b is
-// floor(yc[b][r] m / 2^32) (v_mul_hi_i32_i24 with an SDWA byte destination,
-// the clamped accumulator and m both within 24 signed bits), written
-// byte-major over the four words: a write that keeps the other bytes reads
-// the old word without an interlock, so two such writes to one word need
-// other instructions between them; the closing s_nop covers the first later
-// reader.  The clamps before it are plain code, the first readers of the MFMA
-// results.
-__device__ __forceinline__ void w24_pack16(const int32_t (&yc)[4][4], int32_t m, uint32_t (&w)[4]) {
+// Window path, four words at once: byte r of word a is
+// floor(yc[a][r] m[a] / 2^32) (v_mul_hi_i32_i24 with an SDWA byte
+// destination, the clamped accumulator and m both within 24 signed bits),
+// written byte-major over the four words: a write that keeps the other bytes
+// reads the old word without an interlock, so two such writes to one word
+// need other instructions between them; the closing s_nop covers the first
+// later reader.  The clamps before it are plain code, the first readers of the
+// MFMA results.  (The words' columns may belong to different pairs, so each
+// has its own multiplier.)
+__device__ __forceinline__ void w24_pack4x4(const int32_t (&yc)[4][4], const int32_t (&m)[4], uint32_t (&w)[4]) {
   uint32_t w0, w1, w2, w3;
   asm("v_mul_hi_i32_i24_sdwa %0, %4, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %1, %8, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %2, %12, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %3, %16, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %8, %21 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %12, %22 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %16, %23 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
       "v_mul_hi_i32_i24_sdwa %0, %5, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %1, %9, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %2, %13, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %3, %17, %20 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %9, %21 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %13, %22 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %17, %23 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
       "v_mul_hi_i32_i24_sdwa %0, %6, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %1, %10, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %2, %14, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %3, %18, %20 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %10, %21 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %14, %22 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %18, %23 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
       "v_mul_hi_i32_i24_sdwa %0, %7, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %1, %11, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %2, %15, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
-      "v_mul_hi_i32_i24_sdwa %3, %19, %20 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %1, %11, %21 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %2, %15, %22 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
+      "v_mul_hi_i32_i24_sdwa %3, %19, %23 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD\n\t"
       "s_nop 4"
       : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
       : "v"(yc[0][0]), "v"(yc[0][1]), "v"(yc[0][2]), "v"(yc[0][3]), "v"(yc[1][0]), "v"(yc[1][1]),
         "v"(yc[1][2]), "v"(yc[1][3]), "v"(yc[2][0]), "v"(yc[2][1]), "v"(yc[2][2]), "v"(yc[2][3]),
-        "v"(yc[3][0]), "v"(yc[3][1]), "v"(yc[3][2]), "v"(yc[3][3]), "v"(m));
+        "v"(yc[3][0]), "v"(yc[3][1]), "v"(yc[3][2]), "v"(yc[3][3]), "v"(m[0]), "v"(m[1]), "v"(m[2]),
+        "v"(m[3]));
   w[0] = w0;
   w[1] = w1;
   w[2] = w2;
   w[3] = w3;
 }
 
-template <int TM, int TN, bool W24>
-__device__ __forceinline__ void store_tile_lds(const LinParams& p, const v4i (&acc)[TN][TM],
-                                               int8_t* scr, int m_w, int n_w, int li, int g,
-                                               int lane) {
-  static_assert(16 * TN + 16 == kEpPitch, "pitch");
-  static_assert(64 % TN == 0, "a lane's chunks share one column group");
-  const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
-#pragma unroll
-  for (int a = 0; a < TN; ++a) {
-    const int n = n_w + 16 * a;
-    const int which = qkv ? (n >= p.width) + (n >= 2 * p.width) : 0;
-    if constexpr (W24 && TM == 4) {
-      const int32_t lo = pick3(which, p.ylo[0], p.ylo[1], p.ylo[2]);
-      const int32_t hi = pick3(which, p.yhi[0], p.yhi[1], p.yhi[2]);
-      const int32_t m = pick3(which, p.bm24[0], p.bm24[1], p.bm24[2]);
-      int32_t yc[4][4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          yc[b][r] = __builtin_elementwise_max(__builtin_elementwise_min(acc[a][b][r], hi), lo);
-      uint32_t w[4];
-      w24_pack16(yc, m, w);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = w[b];
-    } else {
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        *(uint32_t*)(scr + (16 * b + li) * kEpPitch + 16 * a + 4 * g) = requant4<W24>(p, which, acc[a][b]);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS (one wave: in order)
-  // lane chunk k: row lane / TN + (64 / TN) k of the block, column group lane % TN
-  const int cg = lane % TN, n = n_w + 16 * cg;
-  int which;
-  const int cofs = col_part(p, qkv, n, which);
-  int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]) + cofs;
-  const bool col_ok = n < p.out_f;
-#pragma unroll
-  for (int k = 0; k < (16 * TM * TN) / 64; ++k) {
-    const int row = lane / TN + (64 / TN) * k, m = m_w + row;
-    const v4i v = *(const v4i*)(scr + row * kEpPitch + 16 * cg);
-    if (m < p.rows && col_ok) *(v4i*)(out + row_offset(p, qkv, m)) = v;
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads are done before the block is reused
-}
-
-// ---------------------------------------------------------------- pipelined GEMM
-// Persistent workgroups (one per CU) of 4 compute waves and kPipeNL loader
-// waves.  The loaders stream 128-byte k-slices of a tile's X rows and W rows
-// (two 64-byte MFMA k-blocks) into a ring of kPipeNS LDS stages with direct
-// global->LDS loads, each loader wave a quarter of every stage (the swizzle is
-// applied on the source side: lane l of a 1 KB block fills LDS bytes
-// [1024 i + 16 l, +16) = (row, chunk position cp) from source chunk
-// cp ^ ((row >> 1) & 7)), kPipeLag stages in flight per wave, running ahead
-// across tile boundaries.  Monotonic LDS counters per stage slot: ready[b]
-// (loader waves that finished a fill), done[b] (compute waves that finished
-// reading it).  Compute waves read a k-block's fragments while the MFMAs of the
-// previous one run.  Tiles are dealt XCD-aware: the workgroups of one XCD
-// (every 8th) take all column tiles of one block of X rows in turn, so those
-// rows reach that XCD's L2 once.
-constexpr int kPipeKB = 128;  // k bytes of a row per stage: whole cache lines per request
-constexpr int kPipeNS = 4;
-constexpr int kPipeLag = 2;
-constexpr int kPipeNL = 4;
-constexpr int kPipeThreads = 64 * (4 + kPipeNL);
-
+// s_waitcnt immediate for vmcnt(n), other counters untouched (n < 64)
 constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+// ---------------------------------------------------------------- tiled GEMM
+// Persistent workgroups of 4 waves, two per CU (so each SIMD runs two waves,
+// one of each workgroup: while one is in its epilogue or at a barrier, the
+// other keeps the matrix core busy).  A workgroup computes BM x BN output
+// tiles, each wave a (BM/2) x (BN/2) quarter: (BM/32) x (BN/32) MFMA tiles of
+// 16 x 16 with their accumulators in VGPRs.  Workgroup w takes the tiles
+// order[w], order[w + G], ... of a table the host builds (see
+// build_tile_order).  The k loop runs over 64-byte k-blocks through a ring of
+// three LDS stages.  Every wave fills its share of a stage with direct
+// global->LDS loads two steps ahead, waits for its own loads of the current
+// stage, and one workgroup barrier per step makes every share visible (and
+// frees the stage read in the step before for refilling).  The direct loads
+// are written in asm: the compiler then does not treat them as LDS writes,
+// which would make it wait for all of them before every operand read; the
+// waits on them are the explicit ones below.  Rows are 64 bytes; the 16-byte
+// chunk c of row r sits at position c ^ ((r >> 1) & 3), so that the b128
+// operand reads (eight lanes per LDS cycle: rows r .. r + 7 of one chunk
+// column) fall on distinct banks.
+constexpr int kTileNS = 3;
+
 template <int BM, int BN>
-struct PipeCfg {
-  static constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave (2 x 2 waves)
-  static constexpr int KB = kPipeKB, NCH = KB / 16, KPS = KB / kStep;  // chunks, k-blocks per stage
-  static constexpr int XB = BM * KB, WB = BN * KB, SB = XB + WB;
-  static constexpr int XI = XB / 1024 / kPipeNL, WI = WB / 1024 / kPipeNL;  // loads per loader wave
-  static constexpr int LDS = kPipeNS * SB + 64 + 4 * (16 * TM) * kEpPitch;  // + epilogue blocks
+struct TileCfg {
+  static constexpr int TMF = BM / 32, TNF = BN / 32;  // X and W fragments of a wave per k-block
+  static constexpr int XB = BM * kStep, WB = BN * kStep, SB = XB + WB;
+  static constexpr int XI = XB / 4096, WI = WB / 4096;  // 1 KB loads per wave and stage
+  static constexpr int L = XI + WI;
 };
 
-__device__ __forceinline__ void pipe_decode(int t, int ntn, int& tm, int& tn) {
-  const int x = t & 7, r = t >> 3, q = r / ntn;
-  tm = q * 8 + x;
-  tn = r - q * ntn;
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at rsrc.base + voff go to LDS
+// at m0 + 16 l (offsets at or past rsrc.num_records read as zeros).  The
+// resource and the LDS address are wave-uniform by construction; the
+// read-first-lane makes that visible to the compiler, which must place them
+// in scalar registers.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
+  v4i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(l) : "memory");
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kPipeThreads) void iqlinear_pipe(LinParams p) {
-  typedef PipeCfg<BM, BN> C;
-  constexpr int TM = C::TM, TN = C::TN, NS = kPipeNS, NL = kPipeNL;
-  static_assert((C::XI + C::WI) * kPipeLag < 64, "vmcnt range");
-  static_assert(C::XI * NL * 1024 == C::XB && C::WI * NL * 1024 == C::WB, "stage split");
-  static_assert(kPipeLag < NS, "ring depth");
-  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  int* const ready = (int*)(smem + NS * C::SB);
-  int* const done = ready + NS;
+__global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
+  typedef TileCfg<BM, BN> C;
+  constexpr int TMF = C::TMF, TNF = C::TNF, XI = C::XI, WI = C::WI, SB = C::SB;
+  static_assert(XI * 4096 == C::XB && WI * 4096 == C::WB, "stage split");
+  static_assert(C::L < 16, "vmcnt range");
+  static_assert(TNF == 4, "one 16-byte output chunk per lane and block");
+  __shared__ __attribute__((aligned(1024))) int8_t sSt[kTileNS * SB];
+  __shared__ __attribute__((aligned(16))) int8_t sEp[4 * 16 * kEpPitch];
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
-  const int G = (int)gridDim.x;
-  const int ntm = (p.rows + BM - 1) / BM, ntn = (p.out_f + BN - 1) / BN;
-  const int total_t = 8 * ntn * ((ntm + 7) / 8);
-  constexpr int KB = C::KB, NCH = C::NCH, KPS = C::KPS;
-  const int nkb = p.in_f / kStep;              // 64-byte k-blocks per tile
-  const int nks = (nkb + KPS - 1) / KPS;       // stages per tile
-  if (tid < NS) {
-    ready[tid] = 0;
-    done[tid] = 0;
-  }
-  __syncthreads();
-  const uint32_t sm0 = lds_addr(smem);
-
-  if (wave >= 4) {
-    // ---- loader wave wl: 1 KB blocks wl, wl + NL, ... of each stage's X and W parts
-    const int wl = wave - 4;
-    const v4i xr = make_rsrc(p.x, (uint32_t)(p.rows * p.in_f));
-    const v4i wr = make_rsrc(p.w, (uint32_t)(p.out_f * p.in_f));
-    auto mark = [&](int step) {
-      if (lane == 0)
-        __hip_atomic_fetch_add(&ready[step % NS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    };
-    int s = 0;
-    for (int t = blockIdx.x; t < total_t; t += G) {
-      int tm, tn;
-      pipe_decode(t, ntn, tm, tn);
-      if (tm >= ntm) continue;
-      const int m0 = tm * BM, n0 = tn * BN;
-      for (int ks = 0; ks < nks; ++ks, ++s) {
-        const int b = s % NS;
-        if (s >= NS) {  // the slot's previous step has been read by every compute wave
-          const int need = 4 * (s / NS);
-          int spins = 0;
-          while (__hip_atomic_load(&done[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
-            if (++spins > p.spin_limit) {
-              lin_giveup(p, 1u);
-              __builtin_amdgcn_s_waitcnt(0);  // no direct loads left in flight
-              return;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
-        const uint32_t sb = sm0 + b * C::SB;
-#pragma unroll
-        for (int j = 0; j < C::XI; ++j) {
-          const int i = wl + NL * j;
-          const int o = 1024 * i + 16 * lane, row = o / KB, cp = (o >> 4) & (NCH - 1);
-          raw_buffer_load_lds(xr, (lds_u32w*)(uintptr_t)(sb + 1024 * i), 16,
-                              (m0 + row) * p.in_f + KB * ks + 16 * (cp ^ ((row >> 1) & (NCH - 1))), 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < C::WI; ++j) {
-          const int i = wl + NL * j;
-          const int o = 1024 * i + 16 * lane, row = o / KB, cp = (o >> 4) & (NCH - 1);
-          raw_buffer_load_lds(wr, (lds_u32w*)(uintptr_t)(sb + C::XB + 1024 * i), 16,
-                              (n0 + row) * p.in_f + KB * ks + 16 * (cp ^ ((row >> 1) & (NCH - 1))), 0, 0, 0);
-        }
-        // this wave's share of the stage issued kPipeLag steps ago has landed
-        if (s >= kPipeLag) {
-          __builtin_amdgcn_s_waitcnt(pipe_vmcnt(kPipeLag * (C::XI + C::WI)));
-          mark(s - kPipeLag);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(pipe_vmcnt(0));
-    for (int q = s - kPipeLag; q < s; ++q)
-      if (q >= 0) mark(q);
-    return;
-  }
-
-  // ---- compute waves: wave (wm, wn) owns rows 16 (TM wm + b) + li and columns
-  //      16 (TN wn + a) + 4 g + r of the tile
   const int wm = wave & 1, wn = wave >> 1;
-  int8_t* const ep_scr = smem + NS * C::SB + 64 + wave * (16 * TM) * kEpPitch;
-  const bool wide_ep = p.layout != IQLINEAR_QKV_HEADS || p.head_dim % 16 == 0;
-  auto wait_ready = [&](int step) -> bool {
-    const int need = NL * (step / NS + 1);
-    int spins = 0;
-    while (__hip_atomic_load(&ready[step % NS], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
-      if (++spins > p.spin_limit) {
-        lin_giveup(p, 2u);
-        return false;
-      }
-      __builtin_amdgcn_s_sleep(1);
+  const int G = (int)gridDim.x;
+  const int ntiles = p.ntiles;
+  const int nkb = p.in_f / kStep;
+  const uint32_t in_f = (uint32_t)p.in_f;
+  const int t0 = blockIdx.x;
+  if (t0 >= ntiles) return;  // uniform over the workgroup, before any barrier
+
+  // ---- loads: this wave's 1 KB blocks (wave, wave + 4, ...) of a stage;
+  //      block i holds rows 16 i .. 16 i + 15; lane l fills row 16 i + l / 4 at
+  //      position l % 4, i.e. source chunk (l % 4) ^ ((l >> 3) & 3) of the
+  //      k-block (the swizzle applied on the source side, since the load writes
+  //      LDS in lane order).  The buffer resource starts at the tile's first
+  //      row and k-block and ends with the operand's last row, so rows past the
+  //      end read as zeros (the range check of a raw buffer covers the
+  //      per-lane offset only).
+  constexpr int NV = XI > WI ? XI : WI;
+  uint32_t voff[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    voff[j] = (uint32_t)(16 * (wave + 4 * j) + (lane >> 2)) * in_f +
+              16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
+  const uint32_t st0 = lds_addr(sSt);
+  int lt = t0, lkb = 0, lst = 0;  // next (tile, k-block) to load, and its stage
+  int2 ltile = p.order[lt];       // (row tile, column tile)
+  auto issue = [&]() __attribute__((always_inline)) {
+    if (lt >= ntiles) return;
+    const uint32_t kofs = (uint32_t)lkb * kStep;
+    const uint32_t x0 = (uint32_t)(ltile.x * BM) * in_f, w0 = (uint32_t)(ltile.y * BN) * in_f;
+    const v4i xr = make_rsrc(p.x + x0 + kofs, (uint32_t)p.rows * in_f - x0 - kofs);
+    const v4i wr = make_rsrc(p.w + w0 + kofs, (uint32_t)p.out_f * in_f - w0 - kofs);
+    const uint32_t sb = st0 + (uint32_t)(lst * SB);
+#pragma unroll
+    for (int j = 0; j < XI; ++j) dma16(xr, voff[j], sb + 1024u * (uint32_t)(wave + 4 * j));
+#pragma unroll
+    for (int j = 0; j < WI; ++j) dma16(wr, voff[j], sb + (uint32_t)C::XB + 1024u * (uint32_t)(wave + 4 * j));
+    lst = lst == kTileNS - 1 ? 0 : lst + 1;
+    if (++lkb == nkb) {
+      lkb = 0;
+      lt += G;
+      if (lt < ntiles) ltile = p.order[lt];
     }
-    return true;
-  };
-  // operand fragments of k-block j of a stage: row r, chunk (4 j + g) ^ swizzle(r)
-  auto lds_off = [&](int r, int j) { return r * KB + 16 * ((4 * j + g) ^ ((r >> 1) & (NCH - 1))); };
-  typedef std::integral_constant<int, 0> J0;
-  typedef std::integral_constant<int, 1> J1;
-  auto read_frags = [&](int step, auto jc, v4i (&fx)[TM], v4i (&fw)[TN]) {
-    constexpr int j = decltype(jc)::value;
-    const int8_t* sb = smem + (step % NS) * C::SB;
-#pragma unroll
-    for (int b = 0; b < TM; ++b) fx[b] = *(const v4i*)(sb + lds_off(16 * (TM * wm + b) + li, j));
-#pragma unroll
-    for (int a = 0; a < TN; ++a) fw[a] = *(const v4i*)(sb + C::XB + lds_off(16 * (TN * wn + a) + li, j));
-  };
-  auto signal_done = [&](int step) {
-    if (lane == 0) __hip_atomic_fetch_add(&done[step % NS], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
 
-  int s = 0;
-  for (int t = blockIdx.x; t < total_t; t += G) {
-    int tm, tn;
-    pipe_decode(t, ntn, tm, tn);
-    if (tm >= ntm) continue;
-    const int m0 = tm * BM, n0 = tn * BN;
-    v4i acc[TN][TM];
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-      for (int b = 0; b < TM; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-    // per stage: block 1's fragments are read while block 0's MFMAs run, the
-    // stage is released once they are in registers, and the next stage's
-    // block 0 is read while block 1's MFMAs run.  The MFMAs of the loop body
-    // are unconditional (a conditional accumulator update makes the compiler
-    // copy every accumulator register each iteration); an odd k-block count
-    // ends with a one-block stage after the loop.
-    v4i fx0[TM], fw0[TN], fx1[TM], fw1[TN];
-    if (!wait_ready(s)) return;
-    read_frags(s, J0(), fx0, fw0);
-    const int nfull = nkb >> 1;  // stages holding two k-blocks
-    for (int st = 0; st < nfull; ++st) {
-      read_frags(s + st, J1(), fx1, fw1);
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw0[a], fx0[b], acc[a][b]);
-      // the MFMAs are issued before the wait (the scheduler would otherwise
-      // hoist the wait above them and expose the fragment reads' latency)
+  // prologue: stages 0 and 1.  The wait of a step counts the loads of the
+  // next stage as the only younger operations; output stores issued in
+  // between only make it wait longer (loads complete in order among
+  // themselves), and a step with no next stage waits for everything.
+  issue();
+  issue();
+  int cst = 0;  // stage of the current step
+  const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
+  const bool wide_ep = !qkv || p.head_dim % 16 == 0;
+  int8_t* const scr = sEp + wave * 16 * kEpPitch;
+
+  for (int t = t0; t < ntiles; t += G) {
+    const int2 tile = p.order[t];
+    const bool last = t + G >= ntiles;
+    v4i acc[TNF][TMF];
+    // one k-step: wait for this wave's loads of the stage, barrier, refill the
+    // stage read in the previous step, then read the operands and multiply
+    // (the first step of a tile starts the accumulators from zero)
+    auto kstep = [&](int kb, auto firstc) __attribute__((always_inline)) {
+      constexpr bool first = decltype(firstc)::value;
+      if (kb + 1 < nkb || !last)
+        __builtin_amdgcn_s_waitcnt(pipe_vmcnt(C::L));
+      else
+        __builtin_amdgcn_s_waitcnt(pipe_vmcnt(0));
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every fragment of the stage is in registers
-      signal_done(s + st);
-      if (st + 1 < nks) {
-        if (!wait_ready(s + st + 1)) return;
-        read_frags(s + st + 1, J0(), fx0, fw0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      issue();
+      const int8_t* const sx = sSt + cst * SB;
+      const int8_t* const sw = sx + C::XB;
+      // fragment rows 16 f + li, chunk g at position g ^ ((li >> 1) & 3)
+      const int cpos = 16 * (g ^ ((li >> 1) & 3));
+      v4i fx[TMF], fw[TNF];
+#pragma unroll
+      for (int a = 0; a < TNF; ++a) fw[a] = *(const v4i*)(sw + (16 * (TNF * wn + a) + li) * kStep + cpos);
+#pragma unroll
+      for (int b = 0; b < TMF; ++b) fx[b] = *(const v4i*)(sx + (16 * (TMF * wm + b) + li) * kStep + cpos);
+#pragma unroll
+      for (int b = 0; b < TMF; ++b)
+#pragma unroll
+        for (int a = 0; a < TNF; ++a)
+          acc[a][b] = mfma64(fw[a], fx[b], first ? v4i{0, 0, 0, 0} : acc[a][b]);
+      cst = cst == kTileNS - 1 ? 0 : cst + 1;
+    };
+    kstep(0, std::true_type());
+    for (int kb = 1; kb < nkb; ++kb) kstep(kb, std::false_type());
+
+    const int m_w = tile.x * BM + 16 * TMF * wm, n_w = tile.y * BN + 16 * TNF * wn;
+    if (!wide_ep) {
+      // head_dim % 16 != 0: each lane stores its 4-byte words directly
+      if (p.w24)
+        store_tile<TMF, TNF, true>(p, acc, m_w + li, n_w + 4 * g);
+      else
+        store_tile<TMF, TNF, false>(p, acc, m_w + li, n_w + 4 * g);
+      continue;
+    }
+    // epilogue: each requantised 16 x 64 block goes through this wave's LDS
+    // rows and leaves as one 16-byte row chunk per lane
+    int32_t lo[TNF], hi[TNF], mm[TNF];
+    int wh[TNF];
+#pragma unroll
+    for (int a = 0; a < TNF; ++a) {
+      const int n = n_w + 16 * a;
+      wh[a] = qkv ? (n >= p.width) + (n >= 2 * p.width) : 0;
+      lo[a] = pick3(wh[a], p.ylo[0], p.ylo[1], p.ylo[2]);
+      hi[a] = pick3(wh[a], p.yhi[0], p.yhi[1], p.yhi[2]);
+      mm[a] = pick3(wh[a], p.bm24[0], p.bm24[1], p.bm24[2]);
+    }
+    const int cg = lane & 3, row = lane >> 2;  // the lane's chunk: row lane / 4, column group lane % 4
+    const int n = n_w + 16 * cg;
+    int which;
+    const int cofs = col_part(p, qkv, n, which);
+    int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]) + cofs;
+    const bool col_ok = n < p.out_f;
+#pragma unroll
+    for (int b = 0; b < TMF; ++b) {
+      uint32_t w[TNF];
+      if (p.w24) {
+        int32_t yc[TNF][4];
+#pragma unroll
+        for (int a = 0; a < TNF; ++a)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            yc[a][r] = __builtin_elementwise_max(__builtin_elementwise_min(acc[a][b][r], hi[a]), lo[a]);
+        w24_pack4x4(yc, mm, w);
+      } else {
+#pragma unroll
+        for (int a = 0; a < TNF; ++a) w[a] = requant4<false>(p, wh[a], acc[a][b]);
       }
 #pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw1[a], fx1[b], acc[a][b]);
-    }
-    if (nkb & 1) {  // the last stage's single k-block is in fx0, fw0
-#pragma unroll
-      for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = mfma64(fw0[a], fx0[b], acc[a][b]);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      signal_done(s + nfull);
-    }
-    s += nks;
-    if (wide_ep) {
-      if (p.w24)
-        store_tile_lds<TM, TN, true>(p, acc, ep_scr, m0 + 16 * TM * wm, n0 + 16 * TN * wn, li, g, lane);
-      else
-        store_tile_lds<TM, TN, false>(p, acc, ep_scr, m0 + 16 * TM * wm, n0 + 16 * TN * wn, li, g, lane);
-    } else {
-      if (p.w24)
-        store_tile<TM, TN, true>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
-      else
-        store_tile<TM, TN, false>(p, acc, m0 + 16 * TM * wm + li, n0 + 16 * TN * wn + 4 * g);
+      for (int a = 0; a < TNF; ++a) *(uint32_t*)(scr + li * kEpPitch + 16 * a + 4 * g) = w[a];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS (one wave: in order)
+      const v4i v = *(const v4i*)(scr + row * kEpPitch + 16 * cg);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the block is rewritten
+      const int m = m_w + 16 * b + row;
+      if (col_ok && m < p.rows) *(v4i*)(out + row_offset(p, qkv, m)) = v;
     }
   }
 }
@@ -462,9 +385,52 @@ using namespace iqattn;
 struct iqlinear_ctx {
   LinParams lp;
   int device;
-  unsigned grid;  // persistent grid of the pipelined kernel
-  uint32_t* status;
+  unsigned grid;  // persistent grid
+  int tile;       // 0: 256 x 128 tiles, 1: 128 x 128 tiles
+  int2* order;    // device copy of the tile table
 };
+
+namespace {
+
+// The tile table: workgroup w runs on XCD w % 8 (workgroups are dealt to the
+// eight XCDs in turn) and takes the table entries w, w + G, w + 2 G, ...  With
+// G a multiple of 8, entry t is computed on XCD t % 8, so the entries
+// t = x + 8 u are XCD x's tiles, in the order u in which its workgroups take
+// them.  Each XCD gets the row tiles r with r % 8 == x, all column tiles of a
+// row tile in a row (so a row tile's X rows reach that XCD's L2 once and are
+// reused from there), up to its share of the table; tiles beyond an XCD's
+// share go, in order, to the XCDs with fewer tiles of their own.  The shares
+// differ by at most one, so every workgroup takes the same number of tiles up
+// to one.
+std::vector<int2> build_tile_order(int ntm, int ntn, unsigned grid) {
+  const int64_t n = (int64_t)ntm * ntn;
+  std::vector<int2> order((size_t)n);
+  if (grid % 8 != 0) {  // small grids (one tile per workgroup): any order
+    for (int64_t t = 0; t < n; ++t) order[(size_t)t] = int2{(int)(t / ntn), (int)(t % ntn)};
+    return order;
+  }
+  std::vector<std::vector<int2>> xt(8);
+  std::vector<int2> spill;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t share = n / 8 + (x < n % 8 ? 1 : 0);
+    for (int r = x; r < ntm; r += 8)
+      for (int c = 0; c < ntn; ++c) {
+        if ((int64_t)xt[x].size() < share)
+          xt[x].push_back(int2{r, c});
+        else
+          spill.push_back(int2{r, c});
+      }
+  }
+  size_t k = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t share = n / 8 + (x < n % 8 ? 1 : 0);
+    while ((int64_t)xt[x].size() < share) xt[x].push_back(spill[k++]);
+    for (size_t u = 0; u < xt[x].size(); ++u) order[(size_t)x + 8 * u] = xt[x][u];
+  }
+  return order;
+}
+
+}  // namespace
 
 extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
   if (!out) return IQATTN_E_NULL;
@@ -542,29 +508,40 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
     lp.seq_magic = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
     lp.seq_shift = l;
   }
-  // persistent kernels: one workgroup per CU, 128 x 128 tiles
+  // persistent grid of two workgroups per CU; the tile shape with the least
+  // work per CU counted in whole rounds of tiles (ties: the larger tile)
   {
-    const int cus = prop.multiProcessorCount;
-    const int64_t tiles = ((int64_t)p->rows + 127) / 128 * ((p->out_features + 127) / 128);
-    c->grid = (unsigned)(tiles < cus ? (tiles > 0 ? tiles : 1) : cus);
-    if (hipFuncSetAttribute((const void*)&iqlinear_pipe<128, 128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            PipeCfg<128, 128>::LDS) != hipSuccess) {
+    const int slots = 2 * prop.multiProcessorCount;
+    const int64_t t256 = ((int64_t)p->rows + 255) / 256 * ((p->out_features + 127) / 128);
+    const int64_t t128 = ((int64_t)p->rows + 127) / 128 * ((p->out_features + 127) / 128);
+    // work per CU in 128 x 128 units; a 128 x 128 tile costs about 1.35 units
+    // (measured: its 64 x 64 wave tiles read more operand bytes per product)
+    const int64_t r256 = (t256 + slots - 1) / slots * 2 * 100, r128 = (t128 + slots - 1) / slots * 135;
+    c->tile = r128 < r256 ? 1 : 0;
+    const int64_t tiles = c->tile ? t128 : t256;
+    if (tiles > INT32_MAX / 2) {
+      free(c);
+      return IQATTN_E_SHAPE;
+    }
+    c->grid = (unsigned)(tiles < slots ? (tiles > 0 ? tiles : 1) : slots);
+    lp.ntiles = (int32_t)tiles;
+  }
+  if (lp.ntiles > 0) {
+    const int bm = c->tile ? 128 : 256;
+    const std::vector<int2> order =
+        build_tile_order((p->rows + bm - 1) / bm, (p->out_features + 127) / 128, c->grid);
+    if (hipMalloc((void**)&c->order, order.size() * sizeof(int2)) != hipSuccess) {
+      free(c);
+      return IQATTN_E_ALLOC;
+    }
+    if (hipMemcpy(c->order, order.data(), order.size() * sizeof(int2), hipMemcpyHostToDevice) !=
+        hipSuccess) {
+      (void)hipFree(c->order);
       free(c);
       return IQATTN_E_DEVICE;
     }
   }
-  if (hipMalloc((void**)&c->status, sizeof(uint32_t)) != hipSuccess) {
-    free(c);
-    return IQATTN_E_ALLOC;
-  }
-  if (hipMemset(c->status, 0, sizeof(uint32_t)) != hipSuccess) {
-    (void)hipFree(c->status);
-    free(c);
-    return IQATTN_E_DEVICE;
-  }
-  lp.status = c->status;
-  lp.spin_limit = 1 << 22;  // polls of about 64 clocks: only a broken invariant gives up
+  lp.order = c->order;
   *out = c;
   return IQATTN_OK;
 }
@@ -584,42 +561,22 @@ extern "C" int iqlinear_forward(iqlinear_ctx* c, const int8_t* x, const int8_t* 
   lp.out[0] = out0;
   lp.out[1] = qkv ? out1 : out0;
   lp.out[2] = qkv ? out2 : out0;
-  constexpr int lds = PipeCfg<128, 128>::LDS;
-  hipLaunchKernelGGL((iqlinear_pipe<128, 128>), dim3(c->grid), dim3(kPipeThreads), lds,
-                     (hipStream_t)hip_stream, lp);
+  if (c->tile)
+    hipLaunchKernelGGL((iqlinear_tile<128, 128>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
+  else
+    hipLaunchKernelGGL((iqlinear_tile<256, 128>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqlinear launch");
   return IQATTN_OK;
 }
 
-extern "C" int iqlinear_check(iqlinear_ctx* c, void* hip_stream) {
-  if (!c) return IQATTN_E_NULL;
-  hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
-  if (e != hipSuccess) return set_hip_error(e, "iqlinear_check synchronize");
-  uint32_t word = 0;
-  if ((e = hipMemcpy(&word, c->status, sizeof(word), hipMemcpyDeviceToHost)) != hipSuccess)
-    return set_hip_error(e, "iqlinear_check read");
-  if (word == 0) return IQATTN_OK;
-  const uint32_t zero = 0;
-  if ((e = hipMemcpy(c->status, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
-    return set_hip_error(e, "iqlinear_check clear");
-  return IQATTN_E_INCOMPLETE;
-}
-
-extern "C" int iqlinear_set_spin_limit(iqlinear_ctx* c, int32_t polls) {
-  if (!c) return IQATTN_E_NULL;
-  if (polls < 1) return IQATTN_E_INVAL;
-  c->lp.spin_limit = polls;
-  return IQATTN_OK;
-}
-
 extern "C" int iqlinear_destroy(iqlinear_ctx* c) {
   if (!c) return IQATTN_OK;
-  if (c->status) {
+  if (c->order) {
     int dev = 0;
     (void)hipGetDevice(&dev);
     (void)hipSetDevice(c->device);
-    (void)hipFree(c->status);
+    (void)hipFree(c->order);
     (void)hipSetDevice(dev);
   }
   free(c);

@@ -39,8 +39,7 @@ IQLINEAR_QKV_HEADS = 1
 
 EXPORTED = ("iqattn_create", "iqattn_forward", "iqattn_destroy", "iqattn_strerror",
             "iqattn_check", "iqattn_set_spin_limit", "iqattn_forward_noalloc",
-            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy", "iqlinear_check",
-            "iqlinear_set_spin_limit",
+            "iqlinear_create", "iqlinear_forward", "iqlinear_destroy",
             "iqgelu_create", "iqgelu_forward", "iqgelu_destroy",
             "iqlayernorm_create", "iqlayernorm_forward", "iqlayernorm_destroy",
             "iqlinattn_create", "iqlinattn_forward", "iqlinattn_destroy")
@@ -112,10 +111,6 @@ def load_library():
         lib.iqlinear_forward.restype = C.c_int
         lib.iqlinear_destroy.argtypes = [C.c_void_p]
         lib.iqlinear_destroy.restype = C.c_int
-        lib.iqlinear_check.argtypes = [C.c_void_p, C.c_void_p]
-        lib.iqlinear_check.restype = C.c_int
-        lib.iqlinear_set_spin_limit.argtypes = [C.c_void_p, C.c_int32]
-        lib.iqlinear_set_spin_limit.restype = C.c_int
         lib.iqgelu_create.argtypes = [C.POINTER(iqgelu_params), C.POINTER(C.c_void_p)]
         lib.iqgelu_create.restype = C.c_int
         lib.iqgelu_forward.argtypes = [C.c_void_p] * 4
@@ -305,19 +300,6 @@ def iqlinear_destroy(ctx: Optional[int]) -> None:
         raise IQAttnError(rc, "iqlinear_destroy")
 
 
-def iqlinear_check(ctx: int, stream=None) -> int:
-    rc = load_library().iqlinear_check(C.c_void_p(ctx), C.c_void_p(_stream_handle(stream)))
-    if rc not in (IQATTN_OK, IQATTN_E_INCOMPLETE):
-        raise IQAttnError(rc, "iqlinear_check")
-    return rc
-
-
-def iqlinear_set_spin_limit(ctx: int, polls: int) -> None:
-    rc = load_library().iqlinear_set_spin_limit(C.c_void_p(ctx), int(polls))
-    if rc != IQATTN_OK:
-        raise IQAttnError(rc, "iqlinear_set_spin_limit")
-
-
 class IQLinear:
     """Owns one linear-layer context: x [rows, in] int8, w [out, in] int8."""
 
@@ -345,11 +327,6 @@ class IQLinear:
         return out
 
     __call__ = forward
-
-    def check(self, stream=None) -> int:
-        """IQATTN_OK, or IQATTN_E_INCOMPLETE if a launch since the last check
-        left output tiles unwritten (synchronises the stream)."""
-        return iqlinear_check(self.ctx, stream)
 
     def close(self):
         if self.ctx:

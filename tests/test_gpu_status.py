@@ -1,7 +1,7 @@
 """Failure path of the kernels' bounded waits, forced from the host.
 
-The work-queue kernels (the specialised attention kernel and the pipelined
-linear layer) wait for their operands with bounded polls.  A test-only spin
+The specialised attention kernel's waves wait for their operands with bounded
+polls (the linear layer's waves meet only at workgroup barriers).  A test-only spin
 limit of one poll makes waves give up while their data is still on the way:
 every kernel must still exit normally, the launch must be reported as
 incomplete by the check call, and the next launch with the default limit
@@ -55,32 +55,6 @@ def test_attention_giveup_is_reported_and_recovers(torch_dev):
     for lo, hi in ((0, 48), (1488, 1536)):
         ref = oracle.forward(w.q, w.k, w.v, w.params, heads=(lo, hi))
         assert np.array_equal(got[lo:hi], ref), (lo, hi)
-
-
-def test_linear_giveup_is_reported_and_recovers(torch_dev):
-    torch = torch_dev
-    from integer_only_quantized_int8_amd import iqattn as IQ
-    lw = W.make_linear(128 * 197, 768, 2304, seed=31, qkv_heads=(128, 197, 12, 64))
-    dev = torch.device("cuda:0")
-    x = torch.from_numpy(lw.x).to(dev)
-    wt = torch.from_numpy(lw.w).to(dev)
-    lin = IQ.IQLinear(lw.params)
-    _say("[status] linear, spin limit 1")
-    IQ.iqlinear_set_spin_limit(lin.ctx, 1)
-    lin.forward(x, wt)
-    assert lin.check() == IQ.IQATTN_E_INCOMPLETE
-    assert lin.check() == IQ.IQATTN_OK
-    _say("[status] linear, default spin limit")
-    IQ.iqlinear_set_spin_limit(lin.ctx, 1 << 22)
-    outs = lin.forward(x, wt)
-    assert lin.check() == IQ.IQATTN_OK
-    C3 = 768
-    for i, o in enumerate(outs):
-        rows = 197 * 2     # the first two images
-        ref = oracle.linear(lw.x[:rows], lw.w[i * C3:(i + 1) * C3], lw.params["b"][i],
-                            lw.params["c"][i]).reshape(2, 197, 12, 64).transpose(0, 2, 1, 3)
-        assert np.array_equal(o.cpu().numpy()[:2], ref), i
-    lin.close()
 
 
 def test_spin_limit_argument_checks(torch_dev):
