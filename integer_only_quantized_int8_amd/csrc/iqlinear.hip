@@ -211,6 +211,21 @@ struct TileCfg {
 // resource and the LDS address are wave-uniform by construction; the
 // read-first-lane makes that visible to the compiler, which must place them
 // in scalar registers.
+// Entry t of the tile table through the scalar cache (a vector load here
+// would make the compiler wait for every direct load in flight, since it
+// counts only its own).  The wait is inside the asm, so the result registers
+// are complete when the compiler first reads them.
+__device__ __forceinline__ int2 tile_entry(const int2* order, int t) {
+  const uint64_t base = (uint64_t)(uintptr_t)order;
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t b1 = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)t * 8u);
+  const uint64_t addr = ((uint64_t)b1 << 32) | b0;
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(addr), "s"(off));
+  return int2{(int)(uint32_t)v, (int)(uint32_t)(v >> 32)};
+}
+
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
   v4i r;
 #pragma unroll
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
               16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
   const uint32_t st0 = lds_addr(sSt);
   int lt = t0, lkb = 0, lst = 0;  // next (tile, k-block) to load, and its stage
-  int2 ltile = p.order[lt];       // (row tile, column tile)
+  int2 ltile = tile_entry(p.order, lt);  // (row tile, column tile)
   auto issue = [&]() __attribute__((always_inline)) {
     if (lt >= ntiles) return;
     const uint32_t kofs = (uint32_t)lkb * kStep;
@@ -272,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
     if (++lkb == nkb) {
       lkb = 0;
       lt += G;
-      if (lt < ntiles) ltile = p.order[lt];
+      if (lt < ntiles) ltile = tile_entry(p.order, lt);
     }
   };
 
@@ -288,12 +303,14 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
   int8_t* const scr = sEp + wave * 16 * kEpPitch;
 
   for (int t = t0; t < ntiles; t += G) {
-    const int2 tile = p.order[t];
+    const int2 tile = tile_entry(p.order, t);
     const bool last = t + G >= ntiles;
     v4i acc[TNF][TMF];
-    // one k-step: wait for this wave's loads of the stage, barrier, refill the
-    // stage read in the previous step, then read the operands and multiply
-    // (the first step of a tile starts the accumulators from zero)
+    // one k-step: wait for this wave's loads of the stage, barrier, read the
+    // operands and multiply (the first step of a tile starts the accumulators
+    // from zero); the refill of the stage read in the previous step goes out
+    // after the first half of the MFMAs, so that the wave does not stall on
+    // issuing loads while its matrix core has no work queued
     auto kstep = [&](int kb, auto firstc) __attribute__((always_inline)) {
       constexpr bool first = decltype(firstc)::value;
       if (kb + 1 < nkb || !last)
@@ -304,7 +321,6 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
-      issue();
       const int8_t* const sx = sSt + cst * SB;
       const int8_t* const sw = sx + C::XB;
       // fragment rows 16 f + li, chunk g at position g ^ ((li >> 1) & 3)
@@ -315,7 +331,15 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
 #pragma unroll
       for (int b = 0; b < TMF; ++b) fx[b] = *(const v4i*)(sx + (16 * (TMF * wm + b) + li) * kStep + cpos);
 #pragma unroll
-      for (int b = 0; b < TMF; ++b)
+      for (int b = 0; b < TMF / 2; ++b)
+#pragma unroll
+        for (int a = 0; a < TNF; ++a)
+          acc[a][b] = mfma64(fw[a], fx[b], first ? v4i{0, 0, 0, 0} : acc[a][b]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = TMF / 2; b < TMF; ++b)
 #pragma unroll
         for (int a = 0; a < TNF; ++a)
           acc[a][b] = mfma64(fw[a], fx[b], first ? v4i{0, 0, 0, 0} : acc[a][b]);
