@@ -206,6 +206,21 @@ def test_shiftmax_close_to_float64_softmax(orc, cfg):
     assert err <= 0.03
 
 
+@pytest.mark.parametrize("N,d", [(641, 64), (777, 32), (1024, 32), (1024, 64)])
+def test_shiftmax_close_to_float64_softmax_long_rows(orc, N, d):
+    """The same 0.03 bound on rows of 641..1024 keys (the longest the boundary
+    accepts): the row sum reaches N * 4096 there, and M = 30 still leaves the
+    IntDiv factor at least 2^8."""
+    w = W.make_workload(1, 2, N, d, seed=N + d)
+    _, dm = orc.forward(w.q, w.k, w.v, w.params, heads=(0, 2), dump=True)
+    L = dm["logit"].astype(np.float64) / w.params["i0"]
+    sm = np.exp(L - L.max(-1, keepdims=True))
+    sm /= sm.sum(-1, keepdims=True)
+    err = np.abs(dm["prob"] / 128.0 - sm).max()
+    print(f"N {N} d {d}: max |P/128 - softmax| = {err:.4f}")
+    assert err <= 0.03
+
+
 # ---------------------------------------------------------------- special cases
 def test_single_token_closed_form(orc):
     """N = 1: the only key holds the whole row, P = 127 (128 clamped), so
@@ -222,7 +237,7 @@ def test_constant_logits_give_uniform_softmax(orc):
     """Q = 0 makes every logit 0: textbook uniform softmax.  P_j is
     floor(floor(2^30 / (N 4096)) 4096 / 2^23) for every key, so the output is the
     requantised column sum of V times that constant."""
-    for N in (1, 2, 7, 49, 197, 577):
+    for N in (1, 2, 7, 49, 197, 577, 641, 1000, 1024):
         w = W.make_workload(1, 1, N, 64, seed=N)
         q0 = np.zeros_like(w.q)
         out = orc.forward(q0, w.k, w.v, w.params)
