@@ -413,7 +413,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
               "the path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
