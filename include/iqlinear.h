@@ -60,7 +60,7 @@ typedef struct iqlinear_ctx iqlinear_ctx;
 
 /* Validate *p and pick the kernel for the current HIP device.  Synchronous;
  * allocates the context and its device tile table (8 bytes per output tile of
- * 256 x 128 or 128 x 128).  *out is NULL on error.                           */
+ * 256 x 256, 256 x 128 or 128 x 128).  *out is NULL on error.                */
 int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out);
 
 /* Enqueue Y = requant(X W^T) on `hip_stream` (a hipStream_t; NULL = null

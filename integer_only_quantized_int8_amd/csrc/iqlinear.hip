@@ -198,11 +198,12 @@ constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // column) fall on distinct banks.
 constexpr int kTileNS = 3;
 
-template <int BM, int BN>
+template <int BM, int BN, int WN>
 struct TileCfg {
-  static constexpr int TMF = BM / 32, TNF = BN / 32;  // X and W fragments of a wave per k-block
+  static constexpr int NW = 2 * WN;                         // waves: 2 along M, WN along N
+  static constexpr int TMF = BM / 32, TNF = BN / (16 * WN);  // X and W fragments of a wave per k-block
   static constexpr int XB = BM * kStep, WB = BN * kStep, SB = XB + WB;
-  static constexpr int XI = XB / 4096, WI = WB / 4096;  // 1 KB loads per wave and stage
+  static constexpr int XI = XB / (1024 * NW), WI = WB / (1024 * NW);  // 1 KB loads per wave and stage
   static constexpr int L = XI + WI;
 };
 
@@ -234,15 +235,15 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(l) : "memory");
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
-  typedef TileCfg<BM, BN> C;
-  constexpr int TMF = C::TMF, TNF = C::TNF, XI = C::XI, WI = C::WI, SB = C::SB;
-  static_assert(XI * 4096 == C::XB && WI * 4096 == C::WB, "stage split");
+template <int BM, int BN, int WN>
+__global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
+  typedef TileCfg<BM, BN, WN> C;
+  constexpr int TMF = C::TMF, TNF = C::TNF, XI = C::XI, WI = C::WI, SB = C::SB, NW = C::NW;
+  static_assert(XI * 1024 * NW == C::XB && WI * 1024 * NW == C::WB, "stage split");
   static_assert(C::L < 16, "vmcnt range");
   static_assert(TNF == 4, "one 16-byte output chunk per lane and block");
   __shared__ __attribute__((aligned(1024))) int8_t sSt[kTileNS * SB];
-  __shared__ __attribute__((aligned(16))) int8_t sEp[4 * 16 * kEpPitch];
+  __shared__ __attribute__((aligned(16))) int8_t sEp[NW * 16 * kEpPitch];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
   uint32_t voff[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j)
-    voff[j] = (uint32_t)(16 * (wave + 4 * j) + (lane >> 2)) * in_f +
+    voff[j] = (uint32_t)(16 * (wave + NW * j) + (lane >> 2)) * in_f +
               16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
   const uint32_t st0 = lds_addr(sSt);
   int lt = t0, lkb = 0, lst = 0;  // next (tile, k-block) to load, and its stage
@@ -280,9 +281,9 @@ __global__ __launch_bounds__(256, 2) void iqlinear_tile(LinParams p) {
     const v4i wr = make_rsrc(p.w + w0 + kofs, (uint32_t)p.out_f * in_f - w0 - kofs);
     const uint32_t sb = st0 + (uint32_t)(lst * SB);
 #pragma unroll
-    for (int j = 0; j < XI; ++j) dma16(xr, voff[j], sb + 1024u * (uint32_t)(wave + 4 * j));
+    for (int j = 0; j < XI; ++j) dma16(xr, voff[j], sb + 1024u * (uint32_t)(wave + NW * j));
 #pragma unroll
-    for (int j = 0; j < WI; ++j) dma16(wr, voff[j], sb + (uint32_t)C::XB + 1024u * (uint32_t)(wave + 4 * j));
+    for (int j = 0; j < WI; ++j) dma16(wr, voff[j], sb + (uint32_t)C::XB + 1024u * (uint32_t)(wave + NW * j));
     lst = lst == kTileNS - 1 ? 0 : lst + 1;
     if (++lkb == nkb) {
       lkb = 0;
@@ -410,7 +411,7 @@ struct iqlinear_ctx {
   LinParams lp;
   int device;
   unsigned grid;  // persistent grid
-  int tile;       // 0: 256 x 128 tiles, 1: 128 x 128 tiles
+  int tile;       // 0: 256 x 128 tiles, 1: 128 x 128, 2: 256 x 256 (8 waves)
   int2* order;    // device copy of the tile table
 };
 
@@ -532,17 +533,28 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
     lp.seq_magic = (uint32_t)(((((uint64_t)1 << l) - d) << 32) / d + 1);
     lp.seq_shift = l;
   }
-  // persistent grid of two workgroups per CU; the tile shape with the least
-  // work per CU counted in whole rounds of tiles (ties: the larger tile)
+  // persistent grid; the tile shape with the least work on the busiest CU:
+  // the most tiles a CU takes (the table balances them to within one) times
+  // the tile's size in 128 x 128 units times a measured cost per unit (the
+  // 8-wave 256 x 256 tile moves the fewest operand bytes per product, the
+  // 128 x 128 tile's 64 x 64 wave tiles the most)
   {
-    const int slots = 2 * prop.multiProcessorCount;
-    const int64_t t256 = ((int64_t)p->rows + 255) / 256 * ((p->out_features + 127) / 128);
-    const int64_t t128 = ((int64_t)p->rows + 127) / 128 * ((p->out_features + 127) / 128);
-    // work per CU in 128 x 128 units; a 128 x 128 tile costs about 1.35 units
-    // (measured: its 64 x 64 wave tiles read more operand bytes per product)
-    const int64_t r256 = (t256 + slots - 1) / slots * 2 * 100, r128 = (t128 + slots - 1) / slots * 135;
-    c->tile = r128 < r256 ? 1 : 0;
-    const int64_t tiles = c->tile ? t128 : t256;
+    const int64_t cus = prop.multiProcessorCount;
+    const int64_t rows = p->rows, n128 = (p->out_features + 127) / 128, n256 = (p->out_features + 255) / 256;
+    const int64_t t[3] = {(rows + 255) / 256 * n128, (rows + 127) / 128 * n128, (rows + 255) / 256 * n256};
+    const int64_t units[3] = {2, 1, 4}, per_unit[3] = {100, 135, 80};
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int k = 0; k < 3; ++k) {
+      const int64_t cost = (t[k] + cus - 1) / cus * units[k] * per_unit[k];
+      if (k == 0 || cost < best_cost) {
+        best = k;
+        best_cost = cost;
+      }
+    }
+    c->tile = best;
+    const int64_t tiles = t[best];
+    const int64_t slots = best == 2 ? cus : 2 * cus;  // one 8-wave or two 4-wave workgroups per CU
     if (tiles > INT32_MAX / 2) {
       free(c);
       return IQATTN_E_SHAPE;
@@ -551,9 +563,9 @@ extern "C" int iqlinear_create(const iqlinear_params* p, iqlinear_ctx** out) {
     lp.ntiles = (int32_t)tiles;
   }
   if (lp.ntiles > 0) {
-    const int bm = c->tile ? 128 : 256;
+    const int bm = c->tile == 1 ? 128 : 256, bn = c->tile == 2 ? 256 : 128;
     const std::vector<int2> order =
-        build_tile_order((p->rows + bm - 1) / bm, (p->out_features + 127) / 128, c->grid);
+        build_tile_order((p->rows + bm - 1) / bm, (p->out_features + bn - 1) / bn, c->grid);
     if (hipMalloc((void**)&c->order, order.size() * sizeof(int2)) != hipSuccess) {
       free(c);
       return IQATTN_E_ALLOC;
@@ -585,10 +597,12 @@ extern "C" int iqlinear_forward(iqlinear_ctx* c, const int8_t* x, const int8_t* 
   lp.out[0] = out0;
   lp.out[1] = qkv ? out1 : out0;
   lp.out[2] = qkv ? out2 : out0;
-  if (c->tile)
-    hipLaunchKernelGGL((iqlinear_tile<128, 128>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
+  if (c->tile == 1)
+    hipLaunchKernelGGL((iqlinear_tile<128, 128, 2>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
+  else if (c->tile == 2)
+    hipLaunchKernelGGL((iqlinear_tile<256, 256, 4>), dim3(c->grid), dim3(512), 0, (hipStream_t)hip_stream, lp);
   else
-    hipLaunchKernelGGL((iqlinear_tile<256, 128>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
+    hipLaunchKernelGGL((iqlinear_tile<256, 128, 2>), dim3(c->grid), dim3(256), 0, (hipStream_t)hip_stream, lp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_hip_error(e, "iqlinear launch");
   return IQATTN_OK;
