@@ -187,12 +187,14 @@ def test_linear_vitb_projections_sampled_rows(torch_dev):
         check(torch_dev, lw, rows=rows, label=name)
 
 
-@pytest.mark.parametrize("rows,fin,fout", [(100864, 768, 2304), (40000, 192, 1040)])
+@pytest.mark.parametrize("rows,fin,fout", [(100864, 768, 2304), (40000, 192, 1040),
+                                           (100864, 192, 1040)])
 def test_linear_many_tiles_per_workgroup(torch_dev, rows, fin, fout):
     # more than twice as many output tiles as the persistent grid has
     # workgroups (up to 14 per workgroup), an odd k-block count and a column
     # count that leaves a partial column tile: the tile table, the load ring
-    # across tile boundaries and the ragged edges, on sampled rows
+    # across tile boundaries and the ragged edges, on sampled rows (the first
+    # and the last shape take 256 x 256 tiles, the second 256 x 128)
     lw = W.make_linear(rows, fin, fout, seed=rows + fin + fout)
     M = lw.params["rows"]
     pick = sorted(set([0, 255, 256, M - 257, M - 1] +
