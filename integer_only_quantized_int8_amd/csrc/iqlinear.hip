@@ -179,11 +179,12 @@ __device__ __forceinline__ void w24_pack4x4(const int32_t (&yc)[4][4], const int
 constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // ---------------------------------------------------------------- tiled GEMM
-// Persistent workgroups of 4 waves, two per CU (so each SIMD runs two waves,
-// one of each workgroup: while one is in its epilogue or at a barrier, the
-// other keeps the matrix core busy).  A workgroup computes BM x BN output
-// tiles, each wave a (BM/2) x (BN/2) quarter: (BM/32) x (BN/32) MFMA tiles of
-// 16 x 16 with their accumulators in VGPRs.  Workgroup w takes the tiles
+// Persistent workgroups of 2 WN waves, each SIMD running two waves: two
+// 4-wave workgroups per CU (while one is in its epilogue or at a barrier, the
+// other keeps the matrix core busy), or one 8-wave workgroup per CU (fewer
+// operand bytes loaded per product).  A workgroup computes BM x BN output
+// tiles, each wave a (BM/2) x (BN/WN) block: (BM/32) x (BN/(16 WN)) MFMA tiles
+// of 16 x 16 with their accumulators in VGPRs.  Workgroup w takes the tiles
 // order[w], order[w + G], ... of a table the host builds (see
 // build_tile_order).  The k loop runs over 64-byte k-blocks through a ring of
 // three LDS stages.  Every wave fills its share of a stage with direct
