@@ -6,8 +6,8 @@
 // (the MSA projections).
 //
 // Kernel (iqlinear_tile below): Y^T = W . X^T with v_mfma_i32_16x16x64_i8,
-// so a lane ends with 4 adjacent output columns of one row; the requantised
-// bytes of 16-row blocks go through LDS and leave as 16-byte row chunks,
+// W rows fed in an order that leaves each lane with 16 adjacent output
+// columns of one row; their requantised bytes leave as one 16-byte store,
 // straight into the head-split layout when asked.
 #include "iqattn_dev.h"
 #include "iqattn.h"
@@ -107,9 +107,9 @@ __device__ __forceinline__ int col_part(const LinParams& p, bool qkv, int n, int
   return h * p.seq_len * p.head_dim + (col - h * p.head_dim);
 }
 
-// Epilogue of one wave's TN x TM accumulator tiles: acc[a][b][r] is output
-// column n + 16 a + r of row m + 16 b; requantised, packed to 4 bytes and
-// stored.  Rows past the end are skipped.
+// Epilogue of one wave's TN x TM accumulator tiles, one 4-byte word at a
+// time: acc[a][b][r] is output column n + 4 a + r of row m + 16 b;
+// requantised, packed to 4 bytes and stored.  Rows past the end are skipped.
 template <int TM, int TN, bool W24>
 __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[TN][TM], int m_base,
                                            int n_base) {
@@ -119,8 +119,8 @@ __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[
   for (int b = 0; b < TM; ++b) rofs[b] = row_offset(p, qkv, m_base + 16 * b);
 #pragma unroll
   for (int a = 0; a < TN; ++a) {
-    const int n = n_base + 16 * a;
-    if (n >= p.out_f) continue;  // out is a multiple of 16: the whole 16-column tile
+    const int n = n_base + 4 * a;
+    if (n >= p.out_f) continue;  // out is a multiple of 16: the lane's whole 16 columns
     int which;
     const int cofs = col_part(p, qkv, n, which);
     int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]);
@@ -132,19 +132,14 @@ __device__ __forceinline__ void store_tile(const LinParams& p, const v4i (&acc)[
   }
 }
 
-// Row pitch of a wave's LDS output block: 64 bytes of a 16 x 64 block plus
-// 16 of padding, which keeps the 4-byte writes of 16 rows bank-conflict free.
-constexpr int kEpPitch = 16 * 4 + 16;
-
 // Window path, four words at once: byte r of word a is
 // floor(yc[a][r] m[a] / 2^32) (v_mul_hi_i32_i24 with an SDWA byte
 // destination, the clamped accumulator and m both within 24 signed bits),
 // written byte-major over the four words: a write that keeps the other bytes
 // reads the old word without an interlock, so two such writes to one word
 // need other instructions between them; the closing s_nop covers the first
-// later reader.  The clamps before it are plain code, the first readers of the
-// MFMA results.  (The words' columns may belong to different pairs, so each
-// has its own multiplier.)
+// later reader.  (Each word takes its own multiplier, so words under
+// different pairs can share a call.)
 __device__ __forceinline__ void w24_pack4x4(const int32_t (&yc)[4][4], const int32_t (&m)[4], uint32_t (&w)[4]) {
   uint32_t w0, w1, w2, w3;
   asm("v_mul_hi_i32_i24_sdwa %0, %4, %20 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD\n\t"
@@ -193,10 +188,16 @@ constexpr int pipe_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // frees the stage read in the step before for refilling).  The direct loads
 // are written in asm: the compiler then does not treat them as LDS writes,
 // which would make it wait for all of them before every operand read; the
-// waits on them are the explicit ones below.  Rows are 64 bytes; the 16-byte
-// chunk c of row r sits at position c ^ ((r >> 1) & 3), so that the b128
-// operand reads (eight lanes per LDS cycle: rows r .. r + 7 of one chunk
-// column) fall on distinct banks.
+// waits on them are the explicit ones below.  Rows are 64 bytes.
+//
+// A wave's W rows enter its MFMAs permuted: fragment a, A-row i is the
+// wave's output column 16 (i / 4) + 4 a + i % 4.  Lane l of an MFMA result
+// holds A-rows 4 (l / 16) .. + 3 of one B-column (an X row), so over the four
+// fragments a lane holds the 16 adjacent output columns 16 (l / 16) .. + 15
+// of one row: its 16 bytes go straight to memory.  The 16-byte chunk c of an
+// X row r sits at position c ^ ((r >> 1) & 3), of a W row at position
+// c ^ (((r >> 1) ^ (2 (r >> 4))) & 3): either way the b128 operand reads
+// (eight lanes per LDS cycle) fall on distinct banks.
 constexpr int kTileNS = 3;
 
 template <int BM, int BN, int WN>
@@ -243,8 +244,8 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
   static_assert(XI * 1024 * NW == C::XB && WI * 1024 * NW == C::WB, "stage split");
   static_assert(C::L < 16, "vmcnt range");
   static_assert(TNF == 4, "one 16-byte output chunk per lane and block");
+  static_assert(NW % 2 == 0, "W block parity is the wave's");
   __shared__ __attribute__((aligned(1024))) int8_t sSt[kTileNS * SB];
-  __shared__ __attribute__((aligned(16))) int8_t sEp[NW * 16 * kEpPitch];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
   //      block i holds rows 16 i .. 16 i + 15; lane l fills row 16 i + l / 4 at
   //      position l % 4, i.e. source chunk (l % 4) ^ ((l >> 3) & 3) of the
   //      k-block (the swizzle applied on the source side, since the load writes
-  //      LDS in lane order).  The buffer resource starts at the tile's first
+  //      LDS in lane order); W rows also flip chunk bit 1 in odd blocks, i.e.
+  //      in the odd waves' blocks.  The buffer resource starts at the tile's first
   //      row and k-block and ends with the operand's last row, so rows past the
   //      end read as zeros (the range check of a raw buffer covers the
   //      per-lane offset only).
@@ -271,6 +273,7 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
   for (int j = 0; j < NV; ++j)
     voff[j] = (uint32_t)(16 * (wave + NW * j) + (lane >> 2)) * in_f +
               16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
+  const uint32_t wflip = 32u * (uint32_t)(wave & 1);
   const uint32_t st0 = lds_addr(sSt);
   int lt = t0, lkb = 0, lst = 0;  // next (tile, k-block) to load, and its stage
   int2 ltile = tile_entry(p.order, lt);  // (row tile, column tile)
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
 #pragma unroll
     for (int j = 0; j < XI; ++j) dma16(xr, voff[j], sb + 1024u * (uint32_t)(wave + NW * j));
 #pragma unroll
-    for (int j = 0; j < WI; ++j) dma16(wr, voff[j], sb + (uint32_t)C::XB + 1024u * (uint32_t)(wave + NW * j));
+    for (int j = 0; j < WI; ++j) dma16(wr, voff[j] ^ wflip, sb + (uint32_t)C::XB + 1024u * (uint32_t)(wave + NW * j));
     lst = lst == kTileNS - 1 ? 0 : lst + 1;
     if (++lkb == nkb) {
       lkb = 0;
@@ -302,7 +305,14 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
   int cst = 0;  // stage of the current step
   const bool qkv = p.layout == IQLINEAR_QKV_HEADS;
   const bool wide_ep = !qkv || p.head_dim % 16 == 0;
-  int8_t* const scr = sEp + wave * 16 * kEpPitch;
+  // this lane's W fragment rows (see the permutation above) and their chunk
+  // positions, as byte offsets in a stage's W part
+  int wofs[TNF];
+#pragma unroll
+  for (int a = 0; a < TNF; ++a) {
+    const int r = 16 * TNF * wn + 16 * (li >> 2) + 4 * a + (li & 3);
+    wofs[a] = r * kStep + 16 * (g ^ (((r >> 1) ^ (2 * (r >> 4))) & 3));
+  }
 
   for (int t = t0; t < ntiles; t += G) {
     const int2 tile = tile_entry(p.order, t);
@@ -325,11 +335,11 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
       asm volatile("" ::: "memory");
       const int8_t* const sx = sSt + cst * SB;
       const int8_t* const sw = sx + C::XB;
-      // fragment rows 16 f + li, chunk g at position g ^ ((li >> 1) & 3)
+      // X fragment rows 16 f + li, chunk g at position g ^ ((li >> 1) & 3)
       const int cpos = 16 * (g ^ ((li >> 1) & 3));
       v4i fx[TMF], fw[TNF];
 #pragma unroll
-      for (int a = 0; a < TNF; ++a) fw[a] = *(const v4i*)(sw + (16 * (TNF * wn + a) + li) * kStep + cpos);
+      for (int a = 0; a < TNF; ++a) fw[a] = *(const v4i*)(sw + wofs[a]);
 #pragma unroll
       for (int b = 0; b < TMF; ++b) fx[b] = *(const v4i*)(sx + (16 * (TMF * wm + b) + li) * kStep + cpos);
 #pragma unroll
@@ -354,29 +364,44 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
     if (!wide_ep) {
       // head_dim % 16 != 0: each lane stores its 4-byte words directly
       if (p.w24)
-        store_tile<TMF, TNF, true>(p, acc, m_w + li, n_w + 4 * g);
+        store_tile<TMF, TNF, true>(p, acc, m_w + li, n_w + 16 * g);
       else
-        store_tile<TMF, TNF, false>(p, acc, m_w + li, n_w + 4 * g);
+        store_tile<TMF, TNF, false>(p, acc, m_w + li, n_w + 16 * g);
       continue;
     }
-    // epilogue: each requantised 16 x 64 block goes through this wave's LDS
-    // rows and leaves as one 16-byte row chunk per lane
-    int32_t lo[TNF], hi[TNF], mm[TNF];
-    int wh[TNF];
-#pragma unroll
-    for (int a = 0; a < TNF; ++a) {
-      const int n = n_w + 16 * a;
-      wh[a] = qkv ? (n >= p.width) + (n >= 2 * p.width) : 0;
-      lo[a] = pick3(wh[a], p.ylo[0], p.ylo[1], p.ylo[2]);
-      hi[a] = pick3(wh[a], p.yhi[0], p.yhi[1], p.yhi[2]);
-      mm[a] = pick3(wh[a], p.bm24[0], p.bm24[1], p.bm24[2]);
-    }
-    const int cg = lane & 3, row = lane >> 2;  // the lane's chunk: row lane / 4, column group lane % 4
-    const int n = n_w + 16 * cg;
+    // epilogue: in block b the lane holds output columns n .. n + 15 of row
+    // m0 + 16 b, all under one pair; requantised, they leave as one 16-byte
+    // store.  The pair's window constants are selected once per tile and kept
+    // in VGPRs (the clamps and multiplies read them as vector operands).
+    const int n = n_w + 16 * g;
     int which;
     const int cofs = col_part(p, qkv, n, which);
-    int8_t* const out = pick3(which, p.out[0], p.out[1], p.out[2]) + cofs;
+    int32_t lo = pick3(which, p.ylo[0], p.ylo[1], p.ylo[2]);
+    int32_t hi = pick3(which, p.yhi[0], p.yhi[1], p.yhi[2]);
+    int32_t mm = pick3(which, p.bm24[0], p.bm24[1], p.bm24[2]);
+    int8_t* outp = pick3(which, p.out[0], p.out[1], p.out[2]) + cofs;
+    asm("" : "+v"(lo), "+v"(hi), "+v"(mm), "+v"(outp));
+    typedef __attribute__((address_space(1))) int8_t gint8;
+    gint8* const out = (gint8*)outp;
+    const int32_t mm4[4] = {mm, mm, mm, mm};
     const bool col_ok = n < p.out_f;
+    // The lane's row in block b is m0 + 16 b: its offset ro is advanced by 16
+    // rows per block (in the head-split layout, a row step that crosses into
+    // the next image also skips the other heads' rows; with at least 16
+    // tokens per image one block crosses at most once).
+    const int m0 = m_w + li;
+    int64_t ro = row_offset(p, qkv, m0);
+    int tk = qkv ? m0 - div_seq(p, m0) * p.seq_len : 0;  // token of row m0 + 16 b
+    const bool inc = !qkv || p.seq_len >= 16;
+    const int64_t step16 = 16 * (int64_t)(qkv ? p.head_dim : p.out_f);
+    const int64_t wrap = qkv ? (int64_t)(p.heads - 1) * p.seq_len * p.head_dim : 0;
+    // The window path's clamps are asm (the compiler would emit min and max:
+    // it cannot tell that the bounds are ordered), and the compiler inserts no
+    // wait states before an asm read of an MFMA result: the last MFMA's result
+    // is complete at most 19 wait states after it issues; the nops give 24.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < TMF; ++b) {
       uint32_t w[TNF];
@@ -386,19 +411,20 @@ __global__ __launch_bounds__(128 * WN, 2) void iqlinear_tile(LinParams p) {
         for (int a = 0; a < TNF; ++a)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            yc[a][r] = __builtin_elementwise_max(__builtin_elementwise_min(acc[a][b][r], hi[a]), lo[a]);
-        w24_pack4x4(yc, mm, w);
+            asm("v_med3_i32 %0, %1, %2, %3" : "=v"(yc[a][r]) : "v"(acc[a][b][r]), "v"(lo), "v"(hi));
+        w24_pack4x4(yc, mm4, w);
       } else {
 #pragma unroll
-        for (int a = 0; a < TNF; ++a) w[a] = requant4<false>(p, wh[a], acc[a][b]);
+        for (int a = 0; a < TNF; ++a) w[a] = requant4<false>(p, which, acc[a][b]);
       }
-#pragma unroll
-      for (int a = 0; a < TNF; ++a) *(uint32_t*)(scr + li * kEpPitch + 16 * a + 4 * g) = w[a];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in LDS (one wave: in order)
-      const v4i v = *(const v4i*)(scr + row * kEpPitch + 16 * cg);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // read before the block is rewritten
-      const int m = m_w + 16 * b + row;
-      if (col_ok && m < p.rows) *(v4i*)(out + row_offset(p, qkv, m)) = v;
+      const int m = m0 + 16 * b;
+      if (col_ok && m < p.rows)
+        *(__attribute__((address_space(1))) v4i*)(out + (inc ? ro : row_offset(p, qkv, m))) =
+            v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      tk += 16;
+      const bool crosses = qkv && tk >= p.seq_len;
+      tk = crosses ? tk - p.seq_len : tk;
+      ro += step16 + (crosses ? wrap : 0);
     }
   }
 }
