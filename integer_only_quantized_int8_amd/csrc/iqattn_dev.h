@@ -255,24 +255,33 @@ __device__ __forceinline__ uint32_t pack4_lowbytes(uint32_t b0, uint32_t b1, uin
 // let the next head's loads run under the current head's compute; the
 // exponential table and the LIS shift scratch follow.
 constexpr int fast_region_bytes(int d, int kt) { return ((kt * 16 * d + 1023) / 1024) * 1024; }
+constexpr int kFastTableBytes = 1024;  // LDS copy of the 256-entry table
 // Rows of up to 256 keys run workgroups of 15 compute waves and one loader
 // wave over four (V, K, Q) buffers (three for the LIS VALU back end, whose
 // shift scratch needs the room); at 197 keys one such workgroup fills a CU,
 // so all waves of a CU share one tile queue (two workgroups on a CU drift
 // apart: the older one's waves win the issue arbitration and the younger one
-// finishes alone).  Longer rows (about 250 VGPRs per lane) use 3 compute waves
-// and one (V, K) buffer, two workgroups per CU.
+// finishes alone).
 // Rows of 209 to 256 keys (14 to 16 tiles) run 11 compute waves over three
 // buffers: at 16 waves their accumulators would not fit the registers, and at
 // d = 64 four buffers would not fit the LDS.
+// Longer rows hold about 250 VGPRs per lane, two waves per SIMD.  When two
+// (V, K) buffers, the table and the LIS shift scratch fit the LDS, one
+// workgroup of 7 compute waves and the loader fills a CU (its waves sit on all
+// four SIMDs); otherwise two workgroups of 3 compute waves and one buffer
+// each share it.
 constexpr bool fast_big(int kt, bool bias) { return kt <= 16; }
 constexpr bool fast_mid(int kt, bool bias) { return kt >= 14 && kt <= 16; }
-constexpr int fast_nbuf(int kt, bool bias, int var) {
-  return fast_big(kt, bias) ? (var == kFastLisValu || fast_mid(kt, bias) ? 3 : 4) : 1;
+constexpr bool fast_long2(int d, int kt, int var) {
+  return kt > 16 && 4 * fast_region_bytes(d, kt) + kFastTableBytes + (var == kFastLisValu ? 7 * 1024 : 0) + 64 <=
+                        160 * 1024;
+}
+constexpr int fast_nbuf(int d, int kt, bool bias, int var) {
+  return fast_big(kt, bias) ? (var == kFastLisValu || fast_mid(kt, bias) ? 3 : 4) : (fast_long2(d, kt, var) ? 2 : 1);
 }
 constexpr int fast_nreg(int kt, bool bias) { return fast_big(kt, bias) ? 3 : 2; }
-constexpr int fast_cw(int kt, bool bias) {
-  return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 11 : 15) : 3;
+constexpr int fast_cw(int d, int kt, bool bias, int var) {
+  return fast_big(kt, bias) ? (fast_mid(kt, bias) ? 11 : 15) : (fast_long2(d, kt, var) ? 7 : 3);
 }
 // minimum waves per SIMD the register allocation must allow
 // (rows of up to 64 keys: 8 waves per SIMD, so that two 16-wave workgroups
@@ -281,7 +290,6 @@ constexpr int fast_cw(int kt, bool bias) {
 constexpr int fast_waves_per_eu(int kt, bool bias) {
   return kt <= 4 ? 8 : (fast_big(kt, bias) ? (fast_mid(kt, bias) ? 3 : 4) : 2);
 }
-constexpr int kFastTableBytes = 1024;  // LDS copy of the 256-entry table
 
 // position of key kappa inside its 64-key block of the staged V^T rows:
 // key 16*tt + 4*g + r sits at byte 16*g + 4*tt + r, so that the P.V MFMA's

@@ -284,11 +284,11 @@ __device__ __forceinline__ void store_out_staged(const DevParams& p, const v4i (
 }
 
 template <int D, int KT, bool BIAS, int VAR>
-__global__ __launch_bounds__(64 * (fast_cw(KT, BIAS) + 1), fast_waves_per_eu(KT, BIAS)) void iqattn_fast(
+__global__ __launch_bounds__(64 * (fast_cw(D, KT, BIAS, VAR) + 1), fast_waves_per_eu(KT, BIAS)) void iqattn_fast(
     DevParams p) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  constexpr int CW = fast_cw(KT, BIAS);         // compute waves; wave CW loads
-  constexpr int NBUF = fast_nbuf(KT, BIAS, VAR);
+  constexpr int CW = fast_cw(D, KT, BIAS, VAR);         // compute waves; wave CW loads
+  constexpr int NBUF = fast_nbuf(D, KT, BIAS, VAR);
   constexpr int R = fast_region_bytes(D, KT);  // bytes of one V, K or Q region
   constexpr int BS = fast_nreg(KT, BIAS) * R;  // bytes of one buffer
   constexpr bool QLDS = fast_nreg(KT, BIAS) == 3;
